@@ -1,0 +1,69 @@
+"""The named synthetic workloads of the attention hot path (shapes, seeds, modes).
+
+Each entry is data only: shapes, seed, dtype, which mask modes are run and how
+the inputs are drawn (see :mod:`online_softmax_flash_amd.inputs`). The scale is
+always 1/sqrt(d), the scaled dot product of the score definition.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str  # "bf16" or "f32"
+    causal: tuple  # mask modes exercised
+    seed: int
+    heavy_frac: float = 0.0
+    backward: bool = False
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def fwd_flops(self, causal: bool) -> float:
+        """Credited forward flops: 4*B*Hq*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2.0 if causal else f
+
+    def bwd_flops(self, causal: bool) -> float:
+        """Credited backward flops (five N^2*d contractions): 10*B*Hq*N^2*d, halved causal."""
+        f = 10.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2.0 if causal else f
+
+    def min_fwd_bytes(self) -> int:
+        """Smallest possible forward HBM traffic: read Q, K, V once, write O and lse once."""
+        e = 2 if self.dtype == "bf16" else 4
+        qo = self.B * self.Hq * self.N * self.d * e
+        kv = self.B * self.Hkv * self.N * self.d * e
+        lse = self.B * self.Hq * self.N * 4
+        return 2 * qo + 2 * kv + lse
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32", 1, 2, 2, 256, 64, "f32", (False,), 0,
+                 note="tiny oracle check, fp32 check mode; also run with Q=0"),
+        Workload("fwd_2k", 4, 32, 32, 2048, 128, "bf16", (False, True), 1),
+        Workload("long_8k", 1, 32, 32, 8192, 128, "bf16", (True,), 2, heavy_frac=0.01,
+                 note="1% of query rows scaled x8"),
+        Workload("long_16k", 1, 32, 32, 16384, 128, "bf16", (True,), 2, heavy_frac=0.01,
+                 note="1% of query rows scaled x8"),
+        Workload("gqa_4k", 2, 32, 8, 4096, 128, "bf16", (True,), 3),
+        Workload("wide_4k", 2, 16, 16, 4096, 256, "bf16", (False,), 3),
+        Workload("bwd_4k", 2, 16, 16, 4096, 128, "bf16", (True,), 4, backward=True),
+    ]
+}
+
+# The workload the headline throughput is quoted on.
+HEADLINE = "long_8k"

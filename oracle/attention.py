@@ -1,0 +1,159 @@
+"""Oracle: exact softmax attention by its definition, in float64 (test infrastructure).
+
+Only tests, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg may
+use this module. It shares no code with the GPU library.
+
+The forward is the plain definition, with the whole score matrix of one
+(batch, head) materialised:
+
+1. scores ``S = scale * Q K^T`` -- mentria.ai "Exact attention, sped up by never
+   writing the giant grid down", card "So don't load it all. Work one block at a
+   time." (the score equation, with scale = 1/sqrt(d) there);
+2. the mask step between scores and softmax -- fanfani.net "FlashAttention",
+   section "The bottleneck was never the arithmetic" (standard pipeline: scores,
+   mask, softmax, multiply by V). The mask is causal: key j is visible to query
+   i iff j <= i; hidden scores are -inf;
+3. the max-subtracted softmax of each row -- mentria.ai, card "But softmax
+   needs the whole row at once." (the softmax equation with m = max_j x_j);
+4. ``O = P V`` -- fanfani.net, same section (multiply by the values);
+5. the saved per-query statistic ``lse = m + ln(l)`` (l = sum of exponentials),
+   which is the pair (m, l) of fanfani.net section "The backward pass, and where
+   the memory saving comes from" folded into one number: P_ij = exp(S_ij - lse_i).
+
+The backward is derived from that definition by the chain rule (the pages only
+say the score blocks are recomputed from the saved statistics):
+``dV = P^T dO``, ``dP = dO V^T``, ``D_i = sum_j P_ij dP_ij``,
+``dS = P * (dP - D)``, ``dQ = scale dS K``, ``dK = scale dS^T Q``. With grouped
+K/V heads (GQA) query head hq reads K/V head ``hq // (Hq / Hkv)`` and dK, dV of
+a K/V head sum over its query heads.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "kv_head",
+    "attn_probs",
+    "attn_fwd_head",
+    "attn_fwd_materialised",
+    "attn_bwd_group",
+    "attn_bwd_analytic",
+]
+
+
+def kv_head(hq: int, Hq: int, Hkv: int) -> int:
+    """K/V head read by query head ``hq``: contiguous groups of Hq/Hkv query heads."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return hq // (Hq // Hkv)
+
+
+def _scores(q_h: np.ndarray, k_h: np.ndarray, scale: float) -> np.ndarray:
+    """S_ij = scale * <q_i, k_j>; rows are queries, columns keys."""
+    return scale * (q_h @ k_h.T)
+
+
+def _visible(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: key j visible to query rows[r]."""
+    if not causal:
+        return np.ones((rows.shape[0], n_keys), dtype=bool)
+    return np.arange(n_keys)[None, :] <= rows[:, None]
+
+
+def _softmax_rows(S: np.ndarray):
+    """Max-subtracted softmax of each row; returns (P, m, l)."""
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])
+    l = E.sum(axis=1)
+    return E / l[:, None], m, l
+
+
+def _rows(rows, n: int) -> np.ndarray:
+    return np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+def attn_probs(q_h, k_h, scale, causal, rows=None) -> np.ndarray:
+    """Attention weights P of one head (rows: query indices, default all)."""
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    r = _rows(rows, q_h.shape[0])
+    S = _scores(q_h[r], k_h, scale)
+    S = np.where(_visible(r, k_h.shape[0], causal), S, -np.inf)
+    P, _, _ = _softmax_rows(S)
+    return P
+
+
+def attn_fwd_head(q_h, k_h, v_h, scale, causal, rows=None):
+    """Forward of one head: returns (O [R, d], lse [R]) for query rows ``rows``."""
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    r = _rows(rows, q_h.shape[0])
+    S = _scores(q_h[r], k_h, scale)
+    S = np.where(_visible(r, k_h.shape[0], causal), S, -np.inf)
+    P, m, l = _softmax_rows(S)
+    return P @ v_h, m + np.log(l)
+
+
+def attn_fwd_materialised(q, k, v, scale, causal, rows=None):
+    """Forward over all heads.
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. Returns O [B, Hq, R, d] and
+    lse [B, Hq, R] (float64) for query rows ``rows`` (default all N).
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    R = N if rows is None else len(rows)
+    O = np.empty((B, Hq, R, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, Hq, R), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            g = kv_head(hq, Hq, Hkv)
+            O[b, hq], lse[b, hq] = attn_fwd_head(q[b, hq], k[b, g], v[b, g], scale, causal, rows)
+    return O, lse
+
+
+def attn_bwd_group(q_g, k_h, v_h, do_g, scale, causal):
+    """Backward of one K/V head and the G query heads that read it.
+
+    q_g, do_g: [G, N, d]; k_h, v_h: [N, d]. Returns dq [G, N, d], dk [N, d],
+    dv [N, d] (float64), the gradients of sum(dO * O).
+    """
+    q_g = np.asarray(q_g, dtype=np.float64)
+    do_g = np.asarray(do_g, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    G, N, _ = q_g.shape
+    dq = np.empty_like(q_g)
+    dk = np.zeros_like(k_h)
+    dv = np.zeros_like(v_h)
+    r = np.arange(N)
+    vis = _visible(r, k_h.shape[0], causal)
+    for j in range(G):
+        S = np.where(vis, _scores(q_g[j], k_h, scale), -np.inf)
+        P, _, _ = _softmax_rows(S)
+        dv += P.T @ do_g[j]
+        dP = do_g[j] @ v_h.T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        dq[j] = scale * (dS @ k_h)
+        dk += scale * (dS.T @ q_g[j])
+    return dq, dk, dv
+
+
+def attn_bwd_analytic(q, k, v, do, scale, causal):
+    """Backward over all heads: returns dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] (float64)."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            dq[b, hs], dk[b, g], dv[b, g] = attn_bwd_group(q[b, hs], k[b, g], v[b, g], do[b, hs], scale, causal)
+    return dq, dk, dv
