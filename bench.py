@@ -1,0 +1,216 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_8k]
+
+One step is one forward pass (scores, mask, online softmax, P V, epilogue) of
+exact attention over one batch of the named synthetic workload, with the
+inputs already resident in device memory. The headline workload is the
+long-context causal forward: B=1, Hq=Hkv=32, N=8192, d=128, bf16 storage,
+fp32 accumulation, 1% of query rows scaled x8, seed 2.
+
+Prints ONE JSON line: throughput in TFLOP/s (credited flops 4*B*Hq*N^2*d,
+halved when causal), the roofline of the forward kernel (MFMA-bound, against
+the 2.5 PFLOP/s dense bf16 peak), the backward pass measured the same way on
+the same inputs, and the CPU oracle timed on a bounded sample of the same
+workload (a baseline only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration runs)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "fwd_long_8k_traffic.json"),
+                    help="HBM bytes per launch from counter runs, if present and current")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, causal, budget_s):
+    """Time the oracle (as it stands) on whole heads of the workload until the budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("internal_api") == "openblas"),
+                      default=os.cpu_count())
+    except Exception:  # threadpoolctl missing: report the host's cores
+        threads = os.cpu_count()
+    G = w.Hq // w.Hkv
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.B * w.Hq:
+        b, hq = divmod(heads, w.Hq)
+        oracle.attn_fwd_head(inp.q[b, hq], inp.k[b, hq // G], inp.v[b, hq // G], w.scale, causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = w.fwd_flops(causal) / (w.B * w.Hq)
+    return {
+        "value": round(per_head * heads / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the same workload, full N x N each, "
+                  f"fp64 numpy, {dt:.1f} s; flops credited as for the GPU",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import online_softmax_flash_amd as fa
+    from online_softmax_flash_amd.inputs import make_inputs
+    from online_softmax_flash_amd.workloads import HEADLINE, WORKLOADS
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    fa.load_library()  # fails loudly when the HIP library is not built
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    causal = w.causal[-1]
+    inp = make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, seed=w.seed, dtype=w.dtype, heavy_frac=w.heavy_frac,
+                      with_dout=not args.no_backward)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (inp.q, inp.k, inp.v))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    fwd = fa.flash_attn_fwd if w.dtype == "bf16" else fa.flash_attn_fwd_f32
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fwd(q, k, v, o, lse, w.scale, causal)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fwd(q, k, v, o, lse, w.scale, causal)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.fwd_flops(causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == w.name and tj.get("kernel_source_sha") == _kernel_sha():
+            traffic = tj.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": causal,
+            "storage": w.dtype, "accumulate": "fp32", "seed": w.seed, "heavy_rows_frac": w.heavy_frac,
+            "credited_flops": flops, "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_kernel<bf16,128,64,causal>",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "min_hbm_bytes": w.min_fwd_bytes(),
+        },
+        "wall_s_timed_region": round(wall_s, 4),
+    }
+
+    if not args.no_backward and inp.do is not None:
+        do = torch.from_numpy(inp.do).to(tdt).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(fa.flash_attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), 256),
+                         dtype=torch.uint8, device=dev)
+        bwd = fa.flash_attn_bwd if w.dtype == "bf16" else fa.flash_attn_bwd_f32
+        try:
+            bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale, causal)
+            torch.cuda.synchronize()
+            nb = max(3, args.steps // 5)
+            ev0.record(stream)
+            for _ in range(nb):
+                bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale, causal)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            bms = ev0.elapsed_time(ev1) / nb
+            btf = w.bwd_flops(causal) / (bms * 1e-3) / 1e12
+            result["backward"] = {"ms": round(bms, 5), "tflops": round(btf, 3), "steps": nb,
+                                  "credited_flops": w.bwd_flops(causal),
+                                  "pct_of_peak": round(100.0 * btf / PEAK_BF16_TFLOPS, 2)}
+        except fa.FlashAttnError as e:
+            result["backward"] = {"error": str(e)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, causal, args.cpu_seconds)
+
+    print(json.dumps(result))
+
+
+def _kernel_sha() -> str:
+    """Hash of the kernel sources, to tell whether stored counter data is current."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "online_softmax_flash_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * flash_attn.h -- C ABI of libflashattn.so: exact softmax attention on one
+ * AMD MI355X (gfx950), computed tile by tile with the online softmax so that
+ * the N x N score matrix never exists in device memory.
+ *
+ * What is computed (per batch b and query head hq, with K/V head
+ * g = hq / (Hq / Hkv)):
+ *   S   = scale * Q K^T                 score equation of mentria.ai "Exact
+ *                                       attention, sped up by never writing the
+ *                                       giant grid down", card "So don't load it
+ *                                       all. Work one block at a time."
+ *   S_ij = -inf for j > i when causal   the mask step of fanfani.net
+ *                                       "FlashAttention", section "The
+ *                                       bottleneck was never the arithmetic"
+ *   P   = row-wise softmax(S)           mentria.ai, card "But softmax needs the
+ *                                       whole row at once."
+ *   O   = P V                           (same fanfani.net section)
+ *   lse = ln(sum_j exp(S_ij))           the per-query statistics kept for the
+ *                                       backward, fanfani.net section "The
+ *                                       backward pass, and where the memory
+ *                                       saving comes from"; P_ij = exp(S_ij - lse_i)
+ * O is reached by the running max / running normaliser / rescaled running
+ * output recurrence of fanfani.net section "A pinch of math: making the
+ * softmax work in pieces", dividing by the normaliser once at the end. The
+ * backward recomputes each score block from Q, K and lse (same "backward
+ * pass" section; synthetic.wiki "FlashAttention: attention's bottleneck is
+ * the wire, not the maths", section "The backward pass buys memory with
+ * recompute") and returns the chain-rule gradients of sum(dO * O).
+ *
+ * Layout: every tensor is dense row-major.
+ *   q, o, dout, dq : [B, Hq,  N, d]
+ *   k, v, dk, dv   : [B, Hkv, N, d]
+ *   lse            : [B, Hq,  N]      float32, natural-log units of the scaled scores
+ * Grouped K/V heads (GQA, MQA when Hkv == 1; synthetic.wiki page, section
+ * "Versions, and what the numbers say"): query head hq reads K/V head
+ * hq / (Hq / Hkv); Hq must be a multiple of Hkv.
+ * Head dims: d in {64, 128, 256} (the same section: head dims up to 256).
+ * Causal mask: key j is visible to query i iff j <= i (0-based, queries and
+ * keys both of length N).
+ *
+ * Element types: the plain entry points take bf16 tensors as raw 16-bit
+ * patterns (uint16 storage; torch.bfloat16 storage is exactly this) and
+ * accumulate in fp32; P is rounded to bf16 (round to nearest even) before the
+ * P V product and O, dq, dk, dv are rounded to bf16 on store. The _f32 entry
+ * points are an fp32 check mode: the same kernels with fp32 storage and fp32
+ * matrix-core products, for tight comparison against a reference.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller (the
+ * backward workspace included). The library never allocates, frees or keeps
+ * device memory and keeps no state between calls: it is reentrant. Outputs
+ * must not alias inputs. All pointers must be 16-byte aligned.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising. The caller orders and
+ * synchronises; the next use of the outputs must be on `stream` or after it.
+ *
+ * Errors: every argument is checked on the host before any HIP call; a
+ * non-zero fa_status is returned and nothing is enqueued. After the launches,
+ * a failing hipGetLastError gives FA_ERR_HIP. Nothing is printed, thrown or
+ * aborted across this boundary. flash_attn_status_str names a status.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* B, Hq, Hkv or N <= 0, Hq % Hkv != 0, or a size overflows int32 indexing */
+  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128, 256}, or causal not 0/1 */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 5,       /* scale is not finite or is negative */
+  FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  FA_ERR_WORKSPACE = 7    /* backward workspace NULL or smaller than flash_attn_bwd_workspace_bytes */
+} fa_status;
+
+/*
+ * Forward, bf16 storage, fp32 accumulation.
+ *   q [B,Hq,N,d], k, v [B,Hkv,N,d]: inputs (bf16 bits).
+ *   o [B,Hq,N,d]: output (bf16 bits).
+ *   lse [B,Hq,N]: output (fp32), ln of the softmax denominator of each row of
+ *     scale*QK^T (masked), i.e. lse_i = max_j S_ij + ln(sum_j exp(S_ij - max_j S_ij)).
+ *   scale: finite, >= 0 (1/sqrt(d) for standard attention; 0 gives uniform weights).
+ *   causal: 0 or 1.
+ * Returns FA_OK or an fa_status (see above).
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/* Forward, fp32 check mode: as flash_attn_fwd with fp32 q, k, v, o. */
+int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these
+ * sizes: 4*B*Hq*N (one fp32 per query row, D_i = sum_c dO_ic O_ic), rounded up
+ * to 256. Linear in N: no N x N buffer. Returns 0 for invalid sizes.
+ */
+size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Backward, bf16 storage, fp32 accumulation. Recomputes every score block from
+ * q, k and the forward's lse; returns the gradients of sum(dout * O).
+ *   q, o, dout [B,Hq,N,d], k, v [B,Hkv,N,d] (bf16 bits), lse [B,Hq,N] fp32:
+ *     the forward's inputs and outputs (o and lse exactly as flash_attn_fwd
+ *     returned them for the same q, k, v, scale, causal).
+ *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]: outputs (bf16 bits); with GQA dk and dv
+ *     of a K/V head sum over its Hq/Hkv query heads.
+ *   workspace: caller-owned device buffer of at least
+ *     flash_attn_bwd_workspace_bytes(B,Hq,Hkv,N,d) bytes; its contents on entry
+ *     are ignored and on return are unspecified.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/* Backward, fp32 check mode: as flash_attn_bwd with fp32 tensors. */
+int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                       const float* dout, float* dq, float* dk, float* dv, void* workspace,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/* Static, NUL-terminated name of a status code ("FA_OK", ...); "FA_UNKNOWN" otherwise. */
+const char* flash_attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,121 @@
+// C ABI of libflashattn.so: argument validation, kernel dispatch, status codes.
+// The operation, layouts, ownership and error conventions are documented in
+// include/flash_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "flash_attn.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point. Element offsets are computed in
+// 64-bit inside the kernels; grid sizes and per-head row indices are 32-bit.
+int check_shape(int B, int Hq, int Hkv, int N, int d, int causal) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * Hq * N;
+  if (rows * (long long)d > ((long long)1 << 40)) return FA_ERR_SHAPE;
+  const long long nqb = (N + 127) / 128;
+  if (nqb * (long long)Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) {
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+int check_ptrs(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] == nullptr) return FA_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!aligned16(ptrs[i])) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int fwd_common(bool f32, const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse};
+  int st = check_ptrs(ptrs, 5);
+  if (st == FA_OK) st = check_shape(B, Hq, Hkv, N, d, causal);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st != FA_OK) return st;
+  const float c = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = f32 ? fa::fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, c, causal, s)
+                           : fa::fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, d, c, causal, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int bwd_common(bool f32, const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  int st = check_ptrs(ptrs, 9);
+  if (st == FA_OK) st = check_shape(B, Hq, Hkv, N, d, causal);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  (void)f32;
+  (void)stream;
+  return FA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  return fwd_common(false, q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream);
+}
+
+int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  return fwd_common(true, q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream);
+}
+
+size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (check_shape(B, Hq, Hkv, N, d, 0) != FA_OK) return 0;
+  const size_t bytes = (size_t)4 * B * Hq * N;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  return bwd_common(false, q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
+                    stream);
+}
+
+int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                       const float* dout, float* dq, float* dk, float* dv, void* workspace,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
+  return bwd_common(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
+                    stream);
+}
+
+const char* flash_attn_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    default: return "FA_UNKNOWN";
+  }
+}
+
+}  // extern "C"

@@ -21,9 +21,11 @@ hand-derived worked examples); see ``tests/test_oracle.py``. No function is
 """
 
 from .attention import (  # noqa: F401
+    attn_fwd_head,
     attn_fwd_materialised,
     attn_probs,
+    attn_bwd_group,
     attn_bwd_analytic,
     kv_head,
 )
-from .online_fold import attn_fwd_online_fold  # noqa: F401
+from .online_fold import attn_fwd_online_fold, fold_head  # noqa: F401

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI: symbols, no device allocation, argument
+validation before any device work. CPU only (no GPU is touched: every call
+below fails validation and returns before any HIP call)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+import online_softmax_flash_amd as fa  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libflashattn.so not built")
+
+FAKE = 0x10000  # non-null, 16-byte aligned; never dereferenced (validation fails first)
+OK_SHAPE = (2, 8, 2, 100, 128)
+STATUS = {"FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3, "FA_ERR_ALIGN": 4,
+          "FA_ERR_SCALE": 5, "FA_ERR_HIP": 6, "FA_ERR_WORKSPACE": 7}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(flash_attn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 6, names
+    lib = fa.load_library()
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), f"{n} not a defined text symbol"
+
+
+def test_no_device_allocation_imports():
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.lib_path()], capture_output=True, text=True).stdout
+    bad = [l for l in out.splitlines() if re.search(r"hip(Ext)?(Malloc|Free|MallocAsync|HostMalloc|MallocManaged)", l)]
+    assert not bad, bad
+
+
+def test_status_strings():
+    for name, code in STATUS.items():
+        assert fa.flash_attn_status_str(code) == name
+    assert fa.flash_attn_status_str(99) == "FA_UNKNOWN"
+
+
+def _fwd(fn="flash_attn_fwd", ptrs=(FAKE,) * 5, shape=OK_SHAPE, scale=0.1, causal=0):
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return getattr(lib, fn)(*p, *shape, ctypes.c_float(scale), causal, None)
+
+
+def _bwd(fn="flash_attn_bwd", ptrs=(FAKE,) * 10, shape=OK_SHAPE, scale=0.1, causal=0):
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return getattr(lib, fn)(*p, *shape, ctypes.c_float(scale), causal, None)
+
+
+@pytest.mark.parametrize("fn", ["flash_attn_fwd", "flash_attn_fwd_f32"])
+def test_forward_validation(fn):
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = 0
+        assert _fwd(fn, ptrs) == STATUS["FA_ERR_NULL"]
+        ptrs[i] = FAKE + 8
+        assert _fwd(fn, ptrs) == STATUS["FA_ERR_ALIGN"]
+    for shape in [(0, 8, 2, 100, 128), (2, 0, 2, 100, 128), (2, 8, 0, 100, 128), (2, 8, 2, 0, 128),
+                  (2, 8, 3, 100, 128), (-1, 8, 2, 100, 128), (1, 1, 1, 2 ** 30, 256)]:
+        assert _fwd(fn, shape=shape) == STATUS["FA_ERR_SHAPE"], shape
+    for d in (0, 32, 96, 100, 512):
+        assert _fwd(fn, shape=(2, 8, 2, 100, d)) == STATUS["FA_ERR_UNSUPPORTED"], d
+    assert _fwd(fn, causal=2) == STATUS["FA_ERR_UNSUPPORTED"]
+    for s in (math.nan, math.inf, -math.inf, -0.5):
+        assert _fwd(fn, scale=s) == STATUS["FA_ERR_SCALE"], s
+
+
+@pytest.mark.parametrize("fn", ["flash_attn_bwd", "flash_attn_bwd_f32"])
+def test_backward_validation(fn):
+    for i in range(9):
+        ptrs = [FAKE] * 10
+        ptrs[i] = 0
+        assert _bwd(fn, ptrs) == STATUS["FA_ERR_NULL"]
+        ptrs[i] = FAKE + 4
+        assert _bwd(fn, ptrs) == STATUS["FA_ERR_ALIGN"]
+    ptrs = [FAKE] * 10
+    ptrs[9] = 0
+    assert _bwd(fn, ptrs) == STATUS["FA_ERR_WORKSPACE"]
+    ptrs[9] = FAKE + 2
+    assert _bwd(fn, ptrs) == STATUS["FA_ERR_ALIGN"]
+    assert _bwd(fn, shape=(2, 8, 3, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _bwd(fn, shape=(2, 8, 2, 100, 48)) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert _bwd(fn, scale=math.nan) == STATUS["FA_ERR_SCALE"]
+
+
+def test_workspace_bytes_linear_in_n():
+    ws = fa.flash_attn_bwd_workspace_bytes
+    assert ws(2, 16, 16, 4096, 128) == 4 * 2 * 16 * 4096
+    assert ws(1, 1, 1, 1, 64) == 256
+    assert ws(1, 2, 1, 1000, 64) == ((4 * 2 * 1000 + 255) // 256) * 256
+    assert ws(2, 16, 16, 8192, 128) == 2 * ws(2, 16, 16, 4096, 128)
+    assert ws(0, 1, 1, 1, 64) == 0
+    assert ws(1, 3, 2, 1, 64) == 0
+    assert ws(1, 1, 1, 1, 100) == 0
