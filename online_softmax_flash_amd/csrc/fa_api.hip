@@ -65,9 +65,13 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
   if (st != FA_OK) return st;
   if (workspace == nullptr) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  (void)f32;
-  (void)stream;
-  return FA_ERR_UNSUPPORTED;
+  const float c = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* dsum = static_cast<float*>(workspace);
+  const hipError_t e =
+      f32 ? fa::bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s)
+          : fa::bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace

@@ -1,0 +1,106 @@
+"""GPU backward parity against the fp64 oracle's analytic gradients, through the C ABI.
+
+The backward consumes the GPU forward's own O and lse, as a caller would.
+Small shapes are compared element by element on dQ, dK and dV (bf16 and the
+fp32 check mode, both mask modes, GQA, ragged tails, every head dim). The
+full-size backward workload (B=2, H=16, N=4096, d=128, causal, seed 4) and
+full-size GQA / wide-head shapes are compared on whole sampled heads, plus
+invariants that hold at any size on every head."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from online_softmax_flash_amd.inputs import make_inputs
+from online_softmax_flash_amd.workloads import WORKLOADS
+from parity_util import announce, assert_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import online_softmax_flash_amd as fa  # noqa: E402
+
+
+def run_fwd_bwd(inp, scale, causal):
+    q, k, v, do = (to_dev(x, inp.dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    o, lse = fa.attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, scale, causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d
+    (1, 2, 2, 1, 64),
+    (1, 2, 1, 17, 64),
+    (2, 4, 2, 255, 128),
+    (1, 2, 2, 300, 128),
+    (1, 4, 1, 1000, 64),
+    (1, 2, 2, 130, 256),
+    (1, 3, 3, 384, 256),
+    (2, 2, 2, 129, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=["x".join(map(str, s)) for s in SMALL])
+def test_bwd_small_full_parity(shape, causal, dtype):
+    B, Hq, Hkv, N, d = shape
+    announce(f"bwd small shape={shape} causal={causal} dtype={dtype} seed=21")
+    inp = make_inputs(B, Hq, Hkv, N, d, seed=21, dtype=dtype, with_dout=True)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = run_fwd_bwd(inp, scale, causal)
+    rq, rk, rv = oracle.attn_bwd_analytic(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    fam = max(float(np.abs(x).max()) for x in (rq, rk, rv))
+    assert_close(from_dev(dq), rq, dtype, f"dQ {shape} causal={causal}", ref_scale=fam)
+    assert_close(from_dev(dk), rk, dtype, f"dK {shape} causal={causal}", ref_scale=fam)
+    assert_close(from_dev(dv), rv, dtype, f"dV {shape} causal={causal}", ref_scale=fam)
+
+
+FULL = [("bwd_4k", True, 3), ("gqa_4k", True, 1), ("wide_4k", False, 1)]
+
+
+@pytest.mark.parametrize("name,causal,groups", FULL, ids=[f[0] for f in FULL])
+def test_bwd_full_size(name, causal, groups):
+    w = WORKLOADS[name]
+    announce(f"bwd full {name} causal={causal} shape=({w.B},{w.Hq},{w.Hkv},{w.N},{w.d}) seed={w.seed}")
+    inp = make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, seed=w.seed, dtype=w.dtype, heavy_frac=w.heavy_frac,
+                      with_dout=True)
+    dq, dk, dv = run_fwd_bwd(inp, w.scale, causal)
+    dq_h, dk_h, dv_h = (from_dev(x) for x in (dq, dk, dv))
+    for x in (dq_h, dk_h, dv_h):
+        assert np.all(np.isfinite(x))
+    G = w.Hq // w.Hkv
+    rng = np.random.default_rng(2000 + w.seed)
+    picks = rng.choice(w.B * w.Hkv, size=groups, replace=False)
+    for p in picks:
+        b, g = divmod(int(p), w.Hkv)
+        hs = slice(g * G, (g + 1) * G)
+        rq, rk, rv = oracle.attn_bwd_group(inp.q[b, hs], inp.k[b, g], inp.v[b, g], inp.do[b, hs], w.scale, causal)
+        assert_close(dq_h[b, hs], rq, "bf16", f"{name} dQ b={b} g={g}")
+        assert_close(dk_h[b, g], rk, "bf16", f"{name} dK b={b} g={g}")
+        assert_close(dv_h[b, g], rv, "bf16", f"{name} dV b={b} g={g}")
+    # Invariants on every K/V head: sum_j dK_j = 0 and sum_j dV_j = sum over the
+    # group's query rows of dO. Bound: bf16 rounding of N stored rows (relative
+    # 2^-9 each, random sign) on top of the fp32 sums.
+    do = inp.do.astype(np.float64).reshape(w.B, w.Hkv, G, w.N, w.d).sum(axis=2)
+    for arr, expect, what in ((dk_h, np.zeros((w.B, w.Hkv, w.d)), "sum dK"),
+                              (dv_h, do.sum(axis=2), "sum dV")):
+        got = arr.sum(axis=2)
+        tol = 8.0 * math.sqrt(w.N) * 2.0 ** -9 * float(np.sqrt(np.mean(arr ** 2))) + 1e-3
+        err = float(np.max(np.abs(got - expect)))
+        assert err <= tol, f"{name} {what}: {err:.3e} > {tol:.3e}"
+
+
+def test_bwd_repeatable():
+    """No atomics: two runs give identical bits."""
+    w = WORKLOADS["bwd_4k"]
+    announce("bwd repeat bwd_4k causal (N=1024 slice)")
+    inp = make_inputs(w.B, w.Hq, w.Hkv, 1024, w.d, seed=w.seed, with_dout=True)
+    a = run_fwd_bwd(inp, w.scale, True)
+    b = run_fwd_bwd(inp, w.scale, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
