@@ -161,7 +161,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_kernel<bf16,128,64,causal>",
+            "kernel": "fwd_bf16_kernel<128,64,8,causal>",
             "achieved": round(tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -94,9 +94,12 @@ __device__ __forceinline__ constexpr int sigma_row(int r, int h) {
 }
 
 // A ROWS x ROW_BYTES tile in LDS, stored in 16-byte chunks with an XOR
-// swizzle. Any 16 lanes that read the same logical chunk of 16 consecutive
-// rows (aligned to 16) touch 16 distinct 16-byte bank groups, i.e. all 64
-// banks once: no conflicts.
+// swizzle of the chunk index by a function of the row. It is chosen so that
+// (a) 16 lanes reading the same logical chunk of 16 consecutive rows (aligned
+// to 16) touch 16 distinct 16-byte bank groups -- all 64 banks once -- and
+// (b) for rows of 256 or 128 bytes, the 4 rows x 32 bytes that 16 lanes of a
+// transposing read fetch (rows 4k..4k+3, logical chunks 2c and 2c+1) land in
+// 8 distinct bank groups.
 template <int ROWS, int ROW_BYTES>
 struct SwzTile {
   static constexpr int kChunks = ROW_BYTES / 16;  // chunks per row
@@ -105,9 +108,20 @@ struct SwzTile {
   static constexpr int kBytes = ROWS * ROW_BYTES;
   static_assert(ROW_BYTES % 16 == 0, "rows must be whole 16-byte chunks");
   static_assert((kM & (kM - 1)) == 0, "chunks per row must be a power of two");
-  __device__ __forceinline__ static int chunk(int row, int ch) {
-    return row * kChunks + (ch ^ (((row / kRowsPer256) ^ (row >> 4)) & (kM - 1)));
+  // XOR applied to the chunk index of row `row` (an involution: applying it
+  // to a physical chunk index gives back the logical one).
+  __device__ __forceinline__ static int xr(int row) {
+    if constexpr (kM == 16) {  // rows of >= 256 bytes: bits (b3 b2 b1 b0) -> (b3 b1 b0 b2)
+      const int r = row & 15;
+      return ((r & 8) | ((r & 3) << 1) | ((r >> 2) & 1)) ^ ((row >> 4) & 15);
+    } else if constexpr (kM == 8) {  // 128-byte rows, two per 256 bytes: u = row/2, (u2 u1 u0) -> (u0 u2 u1)
+      const int u = (row >> 1) & 7;
+      return (((u & 1) << 2) | ((u >> 2) << 1) | ((u >> 1) & 1)) ^ ((row >> 4) & 7);
+    } else {
+      return ((row / kRowsPer256) ^ (row >> 4)) & (kM - 1);
+    }
   }
+  __device__ __forceinline__ static int chunk(int row, int ch) { return row * kChunks + (ch ^ xr(row)); }
   __device__ __forceinline__ static int byte(int row, int ch) { return chunk(row, ch) * 16; }
 };
 
@@ -179,6 +193,45 @@ __device__ __forceinline__ void stage_rows_transposed(uint8_t* lds, const T* g, 
       *reinterpret_cast<T*>(lds + TileT::byte(ch * EPC + i, b / 16) + (b % 16)) = e[i];
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// gfx950 LDS data movers (16-bit elements).
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Copy rows [0, ROWS) of a row-major bf16 matrix (COLS elements per row) into
+// a swizzled LDS tile with direct global->LDS loads (global_load_lds_dwordx4):
+// each lane of a wave writes 16 bytes at LDS base + 16*lane, so the lane's
+// global address is chosen to be the chunk that the swizzled layout puts
+// there. Rows >= valid read row valid-1 instead (finite values; the caller
+// masks them). Completion is tracked by vmcnt; callers wait before reading.
+template <int ROWS, int COLS, int NT>
+__device__ __forceinline__ void dma_rows_bf16(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) {
+  using Tile = SwzTile<ROWS, COLS * 2>;
+  constexpr int CPR = COLS * 2 / 16;
+  constexpr int TOTAL = ROWS * CPR;
+  static_assert(TOTAL % NT == 0, "tile must split evenly over the threads");
+#pragma unroll
+  for (int it = 0; it < TOTAL / NT; ++it) {
+    const int base = it * NT + wave * 64;  // first LDS chunk written by this wave-instruction
+    const int pc = base + lane;
+    const int row = pc / CPR;
+    const int ch = (pc % CPR) ^ Tile::xr(row);
+    const int grow = row < valid ? row : valid - 1;
+    const uint16_t* src = g + (size_t)grow * COLS + ch * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + base * 16), 16, 0, 0);
+  }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 4 elements loaded by lanes
+// 4e + i/4, e = 0..3: if lanes 4e..4e+3 address the 16 consecutive elements
+// of row e of a 4 x 16 block, lane i gets column i of rows 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
 }
 
 }  // namespace fa

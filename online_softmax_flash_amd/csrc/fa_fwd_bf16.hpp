@@ -1,0 +1,369 @@
+// Forward kernel, bf16 storage: the throughput path.
+//
+// Same method as fwd_kernel (fa_fwd.hpp): the online-softmax recurrence of
+// fanfani.net "FlashAttention", section "A pinch of math: making the softmax
+// work in pieces", over one block of queries and a stream of key/value blocks
+// (section "Do not materialize the matrix"). What differs is how the data
+// reaches the matrix cores on gfx950:
+//
+//  * K and V blocks go from global memory straight into LDS
+//    (global_load_lds_dwordx4), double-buffered: block j+1 is in flight while
+//    block j is computed; one barrier per block.
+//  * Both are kept row-major in LDS with padded rows (K: +16 bytes, V: +64
+//    bytes). K is read as the A operand of S^T = K Q^T with 16-byte reads;
+//    V is read as the A operand of O^T = V^T P^T with the transposing read
+//    ds_read_b64_tr_b16, which hands each lane one column of a 4 x 16 block.
+//    The padding makes both access patterns bank-conflict free and every
+//    fragment address a fixed offset from one per-lane base.
+//  * 8 waves x 32 query rows per workgroup (4 for d = 256): each K/V block
+//    staged in LDS serves 256 queries.
+//  * Rescaling is lazy: the reference maximum m used in exp2(s*c - m) is only
+//    raised when a block's maximum exceeds it by more than TAU (log2 units),
+//    so exponentials are at most 2^TAU and the O rescale (and its VALU work)
+//    is skipped for most blocks. The final o / l is unchanged in exact
+//    arithmetic: numerator and denominator always share the same reference.
+//  * Causal: a wave whose 32 queries all precede a block skips its compute
+//    (it still takes part in the block's loads and barrier).
+#pragma once
+
+#include <type_traits>
+
+#include "fa_device.hpp"
+#include "fa_fwd.hpp"
+
+namespace fa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// LDS byte address (as used by ds_* instructions) of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The 2*NT transposing reads (ds_read_b64_tr_b16) that give the NT V fragments
+// of one 16-key chunk, for O^T tiles t = 0..NT-1 (64 bytes apart), each
+// fragment being rows +0..3 and +4..7 (ROWB bytes apart) of the chunk. Issued
+// through inline assembly: the compiler does not insert waits for them, so
+// wait<N>() must be called (LDS operations complete in order: lgkmcnt(N)
+// leaves at most the N most recent ones in flight) before frag() is used.
+template <int NT>
+struct TrReads {
+  s16x4 r[NT][2];
+  template <int OFF, int ROWB>
+  __device__ __forceinline__ void issue(uint32_t addr) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[t][0]) : "v"(addr), "i"(OFF + 64 * t) : "memory");
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r[t][1]) : "v"(addr), "i"(OFF + 64 * t + 4 * ROWB) : "memory");
+    }
+  }
+  template <int N>
+  __device__ __forceinline__ void wait() {
+    constexpr int n = N > 15 ? 15 : N;  // with more in flight, waiting for 15 is stricter, still correct
+    if constexpr (NT == 4) {
+      asm volatile("s_waitcnt lgkmcnt(%8)"
+                   : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]), "+v"(r[2][0]), "+v"(r[2][1]),
+                     "+v"(r[3][0]), "+v"(r[3][1])
+                   : "i"(n));
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[t][0]), "+v"(r[t][1]) : "i"(n));
+    }
+  }
+  __device__ __forceinline__ bf16x8 frag(int t) const {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[t][0], r[t][1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+template <int D, int BN, int NW>
+struct Bf16FwdCfg {
+  static constexpr int BM = 32 * NW;
+  static constexpr int NT = 64 * NW;
+  static constexpr int KROW = 2 * D + 16;  // padded row bytes of the K block
+  static constexpr int VROW = 2 * D + 64;  // padded row bytes of the V block
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = BN * VROW;
+};
+
+// Direct global->LDS copy of rows [0, BN) of a row-major bf16 [*, D] matrix
+// into an LDS block with ROWB-byte rows (2*D data bytes + padding). The block
+// is a sequence of 16-byte slots; wave-instruction n fills slots
+// [64n, 64n + 64), lane i slot 64n + i, and this wave issues instructions
+// n = wave, wave + NW, ... Slots in the padding are skipped (lane inactive).
+template <int D, int BN, int ROWB, int NW>
+struct BlockDma {
+  static constexpr int SPR = ROWB / 16;   // slots per row
+  static constexpr int CPR = 2 * D / 16;  // data slots per row
+  static constexpr int NINSTR = (BN * SPR + 63) / 64;
+  static constexpr int NPER = (NINSTR + NW - 1) / NW;  // instructions per wave (upper bound)
+  int off[NPER];  // element offset of this lane's chunk within the block, or -1
+  int row[NPER];  // its row, for clamping the ragged tail
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int n = wave + j * NW;
+      const int slot = n * 64 + lane;
+      const int r = slot / SPR, c = slot % SPR;
+      const bool ok = n < NINSTR && r < BN && c < CPR;
+      off[j] = ok ? r * D + c * 8 : -1;
+      row[j] = ok ? r : 0;
+    }
+  }
+  // Rows >= valid read row valid - 1 (finite data; the kernel masks those keys).
+  template <bool FULL>
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave) const {
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int n = wave + j * NW;
+      if (j * NW + NW <= NINSTR || n < NINSTR) {  // wave-uniform
+        if (off[j] >= 0) {
+          int e = off[j];
+          if (!FULL && row[j] >= valid) e -= (row[j] - valid + 1) * D;
+          __builtin_amdgcn_global_load_lds(g + e, (lds_void_t*)(lds + n * 1024), 16, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
+  using C = Bf16FwdCfg<D, BN, NW>;
+  constexpr int BM = C::BM;
+  constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
+  constexpr float TAU = 8.0f;
+  constexpr int STAGE = C::KBYTES + C::VBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int nqb = (N + BM - 1) / BM;
+  int b, hq, qb;
+  decode_block(blockIdx.x, a.Hq, a.B, nqb, CAUSAL, b, hq, qb);
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const int q0 = qb * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + li;
+
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (size_t)(b * a.Hq + hq) * N * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + hkv) * N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + hkv) * N * D;
+
+  const int nkb = (N + BN - 1) / BN;
+  const int q_last = min(q0 + BM, N) - 1;
+  const int kb_end = CAUSAL ? min(nkb, q_last / BN + 1) : nkb;
+  // Blocks [0, kb_full) need no mask for any query of the workgroup: every key
+  // is < N and (causal) <= the first query q0.
+  const int kb_full = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+
+  BlockDma<D, BN, C::KROW, NW> kdma;
+  BlockDma<D, BN, C::VROW, NW> vdma;
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
+  const int nfull_rows = N / BN;  // blocks with all BN rows inside [0, N)
+  auto prefetch = [&](int kb) {
+    uint8_t* st = smem + (kb & 1) * STAGE;
+    const uint16_t* kg = K + (size_t)kb * BN * D;
+    const uint16_t* vg = V + (size_t)kb * BN * D;
+    if (kb < nfull_rows) {
+      kdma.template issue<true>(st, kg, BN, wave);
+      vdma.template issue<true>(st + C::KBYTES, vg, BN, wave);
+    } else {
+      kdma.template issue<false>(st, kg, N - kb * BN, wave);
+      vdma.template issue<false>(st + C::KBYTES, vg, N - kb * BN, wave);
+    }
+  };
+  prefetch(0);  // in flight while the query rows are read
+
+  bf16x8 qf[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    qf[f] = (qi < N) ? global_frag<uint16_t>(Q + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = zero16();
+  float m_run = -INFINITY;  // reference maximum of s*c (log2 units)
+  float l_bf = 0.f;         // this lane's share of sum of the bf16-rounded weights (normalises O)
+  float l_32 = 0.f;         // this lane's share of sum of the fp32 weights (gives lse)
+  const float c = a.c;
+
+  // Per-lane byte offsets of the fragment reads.
+  // K (A operand of S^T): row 32*kt + sigma(li), bytes 32*f + 16*h.
+  const int k_off = sigma(li) * C::KROW + 16 * h;
+  // V (A operand of O^T, transposing read): 16-lane group g = lane/16, i = lane%16
+  // reads row 16*kc + 8*h + i/4 (+4 for elements 4..7), column 32*t + 16*(g&1) + 4*(i&3).
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int v_off = C::KBYTES + (8 * h + (i16 >> 2)) * C::VROW + 2 * (16 * (g16 & 1) + 4 * (i16 & 3));
+
+  // One key block: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
+  auto block = [&](int kb, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = kb * BN;
+    if (CAUSAL && k0 > qw0 + 31) return;  // every key of the block follows every query of this wave
+    const uint8_t* st = smem + (kb & 1) * STAGE;
+    f32x16 s[NKT];
+    {
+      bf16x8 kf[NKT][NF];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) kf[kt][f] = *reinterpret_cast<const bf16x8*>(st + k_off + 32 * kt * C::KROW + 32 * f);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        s[kt] = zero16();
+#pragma unroll
+        for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
+      }
+      // Schedule (d <= 128): the first tile's K reads, then each later read
+      // paired with one product, then the remaining products -- reads run
+      // ahead of use. At d = 256 the registers for that are not there.
+      if constexpr (D <= 128) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+#pragma unroll
+        for (int i = 0; i < (NKT - 1) * NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+      }
+    }
+    bool keep[NKT][16];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kt + sigma_row(r, h);
+          keep[kt][r] = key < N && (!CAUSAL || key <= qi);
+          if (!keep[kt][r]) s[kt][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    if (__any(mxc > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mxc);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_bf *= alpha;
+      l_32 *= alpha;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+    }
+    const float base = (m_run == -INFINITY) ? 0.f : m_run;
+    float p32[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -base));
+        if constexpr (MASKED) p = keep[kt][r] ? p : 0.f;
+        s[kt][r] = p;
+        p32[r & 1] += p;
+      }
+    l_32 += p32[0] + p32[1];
+    // P rounded to bf16 (the B operand of P V). O is normalised by the sum of
+    // these same rounded weights (v_dot2 against (1, 1)), so o / l is an exact
+    // convex combination of the weights the matrix cores used.
+    uint32_t pw[NKC][4];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {(__bf16)s[kc >> 1][8 * (kc & 1) + 2 * e], (__bf16)s[kc >> 1][8 * (kc & 1) + 2 * e + 1]};
+        pw[kc][e] = __builtin_bit_cast(uint32_t, pr);
+      }
+    float pbf[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pbf[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kc][e]), kOnesBf16x2, pbf[e & 1], false);
+    l_bf += pbf[0] + pbf[1];
+    // O^T += V^T P^T. The V fragments of chunk kc+1 are requested before the
+    // products of chunk kc; the reads are issued and waited for explicitly
+    // (see TrReads), so the in-flight copy of the next block is never waited on.
+    const uint32_t vaddr = lds_addr(st) + (uint32_t)v_off;
+    constexpr bool VPIPE = D <= 128;  // double-buffer the V fragments (registers permitting)
+    TrReads<NDT> vr[VPIPE ? 2 : 1];
+    vr[0].template issue<0, C::VROW>(vaddr);
+    static_for<0, NKC>([&](auto kcc) {
+      constexpr int kc = decltype(kcc)::value;
+      constexpr int cur = VPIPE ? (kc & 1) : 0;
+      if constexpr (VPIPE && kc + 1 < NKC) {
+        vr[(kc + 1) & 1].template issue<16 * (kc + 1) * C::VROW, C::VROW>(vaddr);
+        vr[cur].template wait<2 * NDT>();
+      } else {
+        if constexpr (!VPIPE && kc > 0) vr[0].template issue<16 * kc * C::VROW, C::VROW>(vaddr);
+        vr[cur].template wait<0>();
+      }
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 w = {pw[kc][0], pw[kc][1], pw[kc][2], pw[kc][3]};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) mma(oacc[t], vr[cur].frag(t), pf);
+    });
+  };
+
+  int kb = 0;
+  for (; kb < kb_full; ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // block kb has landed; every wave is done with block kb-1
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    block(kb, std::false_type{});
+  }
+  for (; kb < kb_end; ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    block(kb, std::true_type{});
+  }
+
+  // Epilogue: divide by the denominator once; lse in natural-log units.
+  const float lb = l_bf + __shfl_xor(l_bf, 32);
+  const float l32 = l_32 + __shfl_xor(l_32, 32);
+  const float inv = 1.f / lb;
+  if (qi < N) {
+    uint16_t* O = static_cast<uint16_t*>(a.o) + (size_t)(b * a.Hq + hq) * N * D + (size_t)qi * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint16_t out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) to_elem(oacc[t][4 * g + e] * inv, out[e]);
+        *reinterpret_cast<uint2*>(O + 32 * t + 8 * g + 4 * h) = *reinterpret_cast<const uint2*>(out);
+      }
+    if (h == 0) a.lse[(size_t)(b * a.Hq + hq) * N + qi] = (m_run + __log2f(l32)) * 0.69314718055994531f;
+  }
+}
+
+template <int D, int BN, int NW, bool CAUSAL>
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  const int nqb = (a.N + BM - 1) / BM;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NW), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa
