@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,8 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "fwd_long_8k_traffic.json"),
-                    help="HBM bytes per launch from counter runs, if present and current")
+    ap.add_argument("--traffic-file", default=None,
+                    help="profile summary holding the HBM bytes per launch from counter runs "
+                         "(default: profiles/fwd_bf16_<workload>.md); used only if its kernel sources match")
     return ap.parse_args()
 
 
@@ -131,14 +133,7 @@ def main():
     flops = w.fwd_flops(causal)
     tflops = flops / (ms * 1e-3) / 1e12
 
-    traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        if tj.get("workload") == w.name and tj.get("kernel_source_sha") == _kernel_sha():
-            traffic = tj.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = _stored_traffic(args.traffic_file or os.path.join(ROOT, "profiles", f"fwd_bf16_{w.name}.md"))
 
     result = {
         "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
@@ -199,6 +194,21 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, inp, causal, args.cpu_seconds)
 
     print(json.dumps(result))
+
+
+def _stored_traffic(path):
+    """HBM bytes per launch recorded by the counter runs in a profile summary,
+    or None when the file is missing or the kernel sources changed since."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    t = re.search(r"^traffic_bytes_per_launch = (\d+)$", text, flags=re.M)
+    k = re.search(r"^kernel_sources_sha = ([0-9a-f]+)$", text, flags=re.M)
+    if not t or not k or k.group(1) != _kernel_sha():
+        return None
+    return int(t.group(1))
 
 
 def _kernel_sha() -> str:
