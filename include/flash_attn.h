@@ -98,8 +98,10 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 /*
  * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these
- * sizes: 4*B*Hq*N (one fp32 per query row, D_i = sum_c dO_ic O_ic), rounded up
- * to 256. Linear in N: no N x N buffer. Returns 0 for invalid sizes.
+ * sizes: two fp32 per query row (D_i = sum_c dO_ic O_ic, and lse_i * log2(e)),
+ * 4*(R64 + R) bytes with R = B*Hq*N and R64 = R rounded up to a multiple of
+ * 64, rounded up to 256. Linear in N: no N x N buffer. Returns 0 for invalid
+ * sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

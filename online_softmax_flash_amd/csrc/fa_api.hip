@@ -90,7 +90,10 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shape(B, Hq, Hkv, N, d, 0) != FA_OK) return 0;
-  const size_t bytes = (size_t)4 * B * Hq * N;
+  // D (fp32 per query row), then lse * log2(e) (fp32 per query row) from the
+  // next 256-byte boundary.
+  const size_t rows = (size_t)B * Hq * N;
+  const size_t bytes = 4 * (((rows + 63) / 64) * 64 + rows);
   return (bytes + 255) & ~(size_t)255;
 }
 

@@ -1,0 +1,378 @@
+// Backward kernels, bf16 storage: the throughput path of the gradients.
+//
+// Same method and the same three launches as fa_bwd.hpp (the gradients of
+// exact softmax attention, every score block recomputed from Q, K and the
+// forward's lse: fanfani.net "FlashAttention", section "The backward pass, and
+// where the memory saving comes from"; synthetic.wiki "FlashAttention:
+// attention's bottleneck is the wire, not the maths", section "The backward
+// pass buys memory with recompute"). What differs is how data reaches the
+// matrix cores on gfx950:
+//
+//  * The streamed tiles (Q and dO in the dK/dV kernel, K and V in the dQ
+//    kernel) go from global memory straight into LDS (global_load_lds),
+//    double-buffered: block i+1 is in flight while block i is computed, one
+//    barrier per block of 64 rows.
+//  * Each tile is stored once, row-major, with rows padded by 16 bytes, and is
+//    read two ways: 16-byte row reads where it is contracted over d (Q K^T,
+//    dO V^T) and transposing reads (ds_read_b64_tr_b16) where it is contracted
+//    over its rows (dO^T P, Q^T dS, K^T dS^T). No transposed copy is made.
+//  * The 32 rows of every score tile are taken in the order rho below. With it
+//    (a) the 16 fp32 accumulator values a lane holds are, as they stand, the
+//    two 8-element fragments of the next product, (b) the 4 rows that one
+//    16-lane group gathers in a transposing read are 4 rows apart, so with
+//    16-byte padding both kinds of read are bank-conflict free, and (c) every
+//    fragment address is a fixed offset from one per-lane base.
+//  * The preprocess also stores lse * log2(e) next to D, so P = exp2(s*c - l2)
+//    costs one fma and one exp per score.
+#pragma once
+
+#include "fa_bwd.hpp"
+#include "fa_fwd_bf16.hpp"
+
+namespace fa {
+
+// Row order of a 32-row score tile: index bits (b4 b3 b2 b1 b0) -> row
+// 16*b4 + 4*(b1 b0) + 2*b3 + b2.
+__device__ __forceinline__ constexpr int rho(int i) {
+  return (i & 16) | ((i & 3) << 2) | (((i >> 3) & 1) << 1) | ((i >> 2) & 1);
+}
+// Row (within the 32-row tile) of accumulator element r of a lane of half h,
+// when the tile's rows were taken in rho order: rho(8*(r/4) + 4*h + r%4).
+__device__ __forceinline__ constexpr int rho_row(int r, int h) {
+  return 16 * (r >> 3) + 4 * (r & 3) + 2 * ((r >> 2) & 1) + h;
+}
+
+// D_i = dO_i . O_i and l2_i = lse_i * log2(e), one row per D/8 threads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdArgs a, float* l2) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const long long rows = (long long)a.B * a.Hq * a.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 of = global_frag<uint16_t>(static_cast<const uint16_t*>(a.o) + row * D + part * 8);
+    const bf16x8 gf = global_frag<uint16_t>(static_cast<const uint16_t*>(a.dout) + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)of[e], (float)gf[e], acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    a.dsum[row] = acc;
+    l2[row] = a.lse[row] * kLog2eF;
+  }
+}
+
+// Direct copy of 64 per-row fp32 values (rows r0 .. r0+63 of one head, taken
+// in rho order within each 32) into 256 bytes of LDS: lane l writes bytes
+// 4l .. 4l+3. Rows >= N read row N-1 (the caller masks them).
+__device__ __forceinline__ void dma_row_stats(uint8_t* lds, const float* g, int r0, int N, int lane) {
+  int r = r0 + 32 * (lane >> 5) + rho(lane & 31);
+  r = r < N ? r : N - 1;
+  __builtin_amdgcn_global_load_lds(g + r, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// Transposing read of a 16-bit fragment: two ds_read_b64_tr_b16, ROWB2 bytes apart.
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int rows_apart_bytes) {
+  const s16x4 lo = lds_read_tr(p);
+  const s16x4 hi = lds_read_tr(p + rows_apart_bytes);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// dK and dV: one workgroup per (block of 32*NW keys, K/V head, batch). Each
+// wave keeps 32 keys of K and V as B-operand fragments in registers and
+// accumulates dK^T and dV^T over every query head of the group and every
+// query block that sees its keys; Q, dO, l2 and D stream through LDS in
+// blocks of 64 queries. No atomics: deterministic.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void bwd_dkdv_bf16_kernel(BwdArgs a, const float* l2g) {
+  constexpr int BKV = 32 * NW, BQ = 64;
+  constexpr int RS = 2 * D + 16;  // padded LDS row bytes
+  constexpr int NF = D / 16, NDT = D / 32;
+  constexpr int TILE = BQ * RS;
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int nkb = (N + BKV - 1) / BKV;
+  int b, hkv, kb;
+  decode_block(blockIdx.x, a.Hkv, a.B, nkb, false, b, hkv, kb);  // key block 0 has the most work
+  const int G = a.Hq / a.Hkv;
+  const int k0 = kb * BKV;
+  const int kw0 = k0 + wave * 32;
+  const int kj = kw0 + li;  // this lane's key
+
+  const size_t kvoff = (size_t)(b * a.Hkv + hkv) * N * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + kvoff;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + kvoff;
+
+  // Q, dO, l2, D of step i (query head g = i / nq, query block qb_start + i % nq).
+  const int nqb = (N + BQ - 1) / BQ;
+  const int qb_start = CAUSAL ? k0 / BQ : 0;
+  const int nq = nqb - qb_start;
+  const int nsteps = G * nq;
+  BlockDma<D, BQ, RS, NW> dma;
+  dma.init(wave, lane);
+  auto prefetch = [&](int i) {
+    const int g = i / nq, q0 = (qb_start + i % nq) * BQ;
+    const size_t qoff = (size_t)(b * a.Hq + hkv * G + g) * N;
+    uint8_t* st = smem + (i & 1) * STAGE;
+    const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + (qoff + q0) * D;
+    const uint16_t* Og = static_cast<const uint16_t*>(a.dout) + (qoff + q0) * D;
+    if (q0 + BQ <= N) {
+      dma.template issue<true>(st, Qg, BQ, wave);
+      dma.template issue<true>(st + TILE, Og, BQ, wave);
+    } else {
+      dma.template issue<false>(st, Qg, N - q0, wave);
+      dma.template issue<false>(st + TILE, Og, N - q0, wave);
+    }
+    if (wave == 0) dma_row_stats(st + 2 * TILE, l2g + qoff, q0, N, lane);
+    if (wave == NW - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qoff, q0, N, lane);
+  };
+  if (nsteps > 0) prefetch(0);
+
+  bf16x8 kf[NF], vf[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    kf[f] = (kj < N) ? global_frag<uint16_t>(K + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    vf[f] = (kj < N) ? global_frag<uint16_t>(V + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+  }
+  f32x16 dk_acc[NDT], dv_acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    dk_acc[t] = zero16();
+    dv_acc[t] = zero16();
+  }
+  const float c = a.c;
+  // Per-lane byte offsets: row reads (A operand, row rho(li), bytes 32f + 16h)
+  // and transposing reads (16-lane group g16 gathers rows 4e + h (+2) of a
+  // 16-row chunk, columns 32t + 16*(g16&1) + 4*(i16&3) .. +3).
+  const int row_off = rho(li) * RS + 16 * h;
+  const int tr_off = (4 * (i16 >> 2) + h) * RS + 32 * (g16 & 1) + 8 * (i16 & 3);
+
+  for (int i = 0; i < nsteps; ++i) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // step i has landed; every wave is done with step i-1
+    if (i + 1 < nsteps) prefetch(i + 1);
+    const int q0 = (qb_start + i % nq) * BQ;
+    const uint8_t* st = smem + (i & 1) * STAGE;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs0 = q0 + 32 * sub;
+      if (qs0 >= N) break;
+      if (CAUSAL && qs0 + 31 < kw0) continue;  // every key of this wave follows every query
+      const uint8_t* qs = st + sub * 32 * RS;
+      const uint8_t* os = qs + TILE;
+      const float* l2s = reinterpret_cast<const float*>(st + 2 * TILE) + 32 * sub;
+      const float* ds_s = l2s + BQ;
+      // S = Q K^T and dP = dO V^T: rows = queries (rho order), column = key li.
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(qs + row_off + 32 * f), kf[f]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) mma(dp, *reinterpret_cast<const bf16x8*>(os + row_off + 32 * f), vf[f]);
+      const bool masked = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N;
+      float p[16], ds[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 8 * r4 + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds_s + 8 * r4 + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e]));
+          if (masked) {
+            const int qr = qs0 + rho_row(r, h);
+            if (qr >= N || (CAUSAL && kj > qr)) pv = 0.f;
+          }
+          p[r] = pv;
+          ds[r] = pv * (dp[r] - d4[e]);
+        }
+      }
+      bf16x8 pf[2], dsf[2];
+      pack_frag(pf[0], p);
+      pack_frag(pf[1], p + 8);
+      pack_frag(dsf[0], ds);
+      pack_frag(dsf[1], ds + 8);
+      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+          mma(dv_acc[t], tr_frag(os + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), pf[c2]);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+          mma(dk_acc[t], tr_frag(qs + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), dsf[c2]);
+    }
+  }
+
+  if (kj < N) {
+    uint16_t* dK = static_cast<uint16_t*>(a.dk) + kvoff + (size_t)kj * D;
+    uint16_t* dV = static_cast<uint16_t*>(a.dv) + kvoff + (size_t)kj * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint16_t ok[4], ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          to_elem(dk_acc[t][4 * gq + e] * a.scale, ok[e]);
+          to_elem(dv_acc[t][4 * gq + e], ov[e]);
+        }
+        const int col = 32 * t + 8 * gq + 4 * h;
+        *reinterpret_cast<uint2*>(dK + col) = *reinterpret_cast<const uint2*>(ok);
+        *reinterpret_cast<uint2*>(dV + col) = *reinterpret_cast<const uint2*>(ov);
+      }
+  }
+}
+
+// dQ: one workgroup per (block of 32*NW queries, query head, batch). Each wave
+// keeps 32 query rows of Q and dO as B-operand fragments in registers and
+// accumulates dQ^T over the visible key blocks; K and V stream through LDS in
+// blocks of 64 keys.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const float* l2g) {
+  constexpr int BM = 32 * NW, BK = 64;
+  constexpr int RS = 2 * D + 16;
+  constexpr int NF = D / 16, NDT = D / 32;
+  constexpr int TILE = BK * RS;
+  constexpr int STAGE = 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int nqb = (N + BM - 1) / BM;
+  int b, hq, qb;
+  decode_block(blockIdx.x, a.Hq, a.B, nqb, CAUSAL, b, hq, qb);
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const int q0 = qb * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + li;
+
+  const size_t qoff = (size_t)(b * a.Hq + hq) * N;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + qoff * D;
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + qoff * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + hkv) * N * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + hkv) * N * D;
+
+  const int nkb = (N + BK - 1) / BK;
+  const int q_last = min(q0 + BM, N) - 1;
+  const int kb_end = CAUSAL ? min(nkb, q_last / BK + 1) : nkb;
+  BlockDma<D, BK, RS, NW> dma;
+  dma.init(wave, lane);
+  auto prefetch = [&](int kb) {
+    uint8_t* st = smem + (kb & 1) * STAGE;
+    const uint16_t* kg = K + (size_t)kb * BK * D;
+    const uint16_t* vg = V + (size_t)kb * BK * D;
+    if ((kb + 1) * BK <= N) {
+      dma.template issue<true>(st, kg, BK, wave);
+      dma.template issue<true>(st + TILE, vg, BK, wave);
+    } else {
+      dma.template issue<false>(st, kg, N - kb * BK, wave);
+      dma.template issue<false>(st + TILE, vg, N - kb * BK, wave);
+    }
+  };
+  if (kb_end > 0) prefetch(0);
+
+  bf16x8 qf[NF], of[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    qf[f] = (qi < N) ? global_frag<uint16_t>(Q + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    of[f] = (qi < N) ? global_frag<uint16_t>(dO + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+  }
+  const float l2 = (qi < N) ? l2g[qoff + qi] : INFINITY;
+  const float Di = (qi < N) ? a.dsum[qoff + qi] : 0.f;
+  f32x16 dq_acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) dq_acc[t] = zero16();
+  const float c = a.c;
+  const int row_off = rho(li) * RS + 16 * h;
+  const int tr_off = (4 * (i16 >> 2) + h) * RS + 32 * (g16 & 1) + 8 * (i16 & 3);
+
+  for (int kb = 0; kb < kb_end; ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    const uint8_t* st = smem + (kb & 1) * STAGE;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int ks0 = kb * BK + 32 * sub;
+      if (ks0 >= N) break;
+      if (CAUSAL && ks0 > qw0 + 31) continue;  // every key follows every query of this wave
+      const uint8_t* ks = st + sub * 32 * RS;
+      const uint8_t* vs = ks + TILE;
+      // S^T = K Q^T and dP^T = V dO^T: rows = keys (rho order), column = query li.
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(ks + row_off + 32 * f), qf[f]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) mma(dp, *reinterpret_cast<const bf16x8*>(vs + row_off + 32 * f), of[f]);
+      const bool masked = (CAUSAL && ks0 + 31 > qw0) || ks0 + 32 > N;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
+        if (masked) {
+          const int key = ks0 + rho_row(r, h);
+          if (key >= N || (CAUSAL && key > qi)) pv = 0.f;
+        }
+        ds[r] = pv * (dp[r] - Di);
+      }
+      bf16x8 dsf[2];
+      pack_frag(dsf[0], ds);
+      pack_frag(dsf[1], ds + 8);
+      // dQ^T += K^T dS^T (contraction over the 32 keys).
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+          mma(dq_acc[t], tr_frag(ks + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), dsf[c2]);
+    }
+  }
+
+  if (qi < N) {
+    uint16_t* dQ = static_cast<uint16_t*>(a.dq) + (qoff + qi) * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint16_t out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) to_elem(dq_acc[t][4 * gq + e] * a.scale, out[e]);
+        *reinterpret_cast<uint2*>(dQ + 32 * t + 8 * gq + 4 * h) = *reinterpret_cast<const uint2*>(out);
+      }
+  }
+}
+
+// Workspace layout of the bf16 backward: D [B*Hq*N] fp32, then l2 [B*Hq*N]
+// fp32 starting at the next 256-byte boundary.
+inline size_t bwd_l2_offset_floats(long long rows) { return (size_t)((rows + 63) / 64) * 64; }
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  constexpr int NWKV = 4, NWQ = 4;
+  const long long rows = (long long)a.B * a.Hq * a.N;
+  float* l2 = a.dsum + bwd_l2_offset_floats(rows);
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a,
+                     l2);
+  const int nkb = (a.N + 32 * NWKV - 1) / (32 * NWKV);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(64 * NWKV), 0,
+                     stream, a, (const float*)l2);
+  const int nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NWQ), 0,
+                     stream, a, (const float*)l2);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -102,9 +102,10 @@ def test_backward_validation(fn):
 
 def test_workspace_bytes_linear_in_n():
     ws = fa.flash_attn_bwd_workspace_bytes
-    assert ws(2, 16, 16, 4096, 128) == 4 * 2 * 16 * 4096
-    assert ws(1, 1, 1, 1, 64) == 256
-    assert ws(1, 2, 1, 1000, 64) == ((4 * 2 * 1000 + 255) // 256) * 256
+    # two fp32 per query row: D, then lse * log2(e) from a 64-row boundary
+    assert ws(2, 16, 16, 4096, 128) == 8 * 2 * 16 * 4096
+    assert ws(1, 1, 1, 1, 64) == 512
+    assert ws(1, 2, 1, 1000, 64) == ((4 * (2048 + 2000) + 255) // 256) * 256
     assert ws(2, 16, 16, 8192, 128) == 2 * ws(2, 16, 16, 4096, 128)
     assert ws(0, 1, 1, 1, 64) == 0
     assert ws(1, 3, 2, 1, 64) == 0
