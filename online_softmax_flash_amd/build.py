@@ -23,6 +23,8 @@ ARCH = "gfx950"
 
 # No packed fp32 arithmetic (v_pk_*_f32) in device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source additions: the bf16 dQ kernel keeps its MFMA accumulators in VGPRs.
+EXTRA_FLAGS = {"fa_bwd_dq_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"]
 
@@ -40,7 +42,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -81,22 +81,36 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int rows_apart_bytes
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// dK and dV: one workgroup per (block of 32*NW keys, K/V head, batch). Each
-// wave keeps 32 keys of K and V as B-operand fragments in registers and
-// accumulates dK^T and dV^T over every query head of the group and every
-// query block that sees its keys; Q, dO, l2 and D stream through LDS in
-// blocks of 64 queries. No atomics: deterministic.
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void bwd_dkdv_bf16_kernel(BwdArgs a, const float* l2g) {
-  constexpr int BKV = 32 * NW, BQ = 64;
+// dK and dV: one workgroup per (block of 32*NP keys, K/V head, batch), with
+// 2*NP waves in NP pairs; pair p owns keys k0 + 32p .. +31 and splits the
+// work of each 32-query subtile between its two waves:
+//   wave p      ("P wave"):  S = Q K^T, P = exp2(S*c - l2) (masked), P -> LDS,
+//                            then dV^T += dO^T P;            K and dV^T resident;
+//   wave p + NP ("dS wave"): dP = dO V^T, then (P from LDS) dS = P (dP - D),
+//                            dK^T += Q^T dS;                 V and dK^T resident.
+// Each wave does 16 of the pair's 32 products per subtile and holds half of
+// the pair's registers, so two waves fit on each SIMD and the softmax work of
+// one overlaps the products of the other. Per block of 64 queries: barrier 1
+// (block landed, previous block done), the P waves write P, barrier 2 (P
+// visible), the products that need P. Q, dO, l2 and D stream through LDS in
+// double-buffered blocks. No atomics: deterministic.
+template <int D, int NP, bool CAUSAL>
+__global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, const float* l2g) {
+  constexpr int NW = 2 * NP;
+  constexpr int BKV = 32 * NP, BQ = 64;
   constexpr int RS = 2 * D + 16;  // padded LDS row bytes
   constexpr int NF = D / 16, NDT = D / 32;
   constexpr int TILE = BQ * RS;
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int PX = 2 * 64 * 16 * 4;  // P exchange bytes per pair: 2 subtiles x 64 lanes x 16 fp32
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + NP * PX];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
 
   const int N = a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wave < NP;
+  const int pair = pwave ? wave : wave - NP;
   const int h = lane >> 5, li = lane & 31;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int nkb = (N + BKV - 1) / BKV;
@@ -104,12 +118,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_bf16_kernel(BwdArgs a, const
   decode_block(blockIdx.x, a.Hkv, a.B, nkb, false, b, hkv, kb);  // key block 0 has the most work
   const int G = a.Hq / a.Hkv;
   const int k0 = kb * BKV;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + pair * 32;
   const int kj = kw0 + li;  // this lane's key
 
   const size_t kvoff = (size_t)(b * a.Hkv + hkv) * N * D;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + kvoff;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + kvoff;
 
   // Q, dO, l2, D of step i (query head g = i / nq, query block qb_start + i % nq).
   const int nqb = (N + BQ - 1) / BQ;
@@ -136,100 +148,131 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_bf16_kernel(BwdArgs a, const
   };
   if (nsteps > 0) prefetch(0);
 
-  bf16x8 kf[NF], vf[NF];
+  // This wave's resident operand: K (P wave) or V (dS wave), 32 keys, as
+  // B-operand fragments; and its accumulator, dV^T or dK^T.
+  const uint16_t* KV = static_cast<const uint16_t*>(pwave ? a.k : a.v) + kvoff;
+  bf16x8 kvf[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    kf[f] = (kj < N) ? global_frag<uint16_t>(K + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
-    vf[f] = (kj < N) ? global_frag<uint16_t>(V + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
-  }
-  f32x16 dk_acc[NDT], dv_acc[NDT];
+  for (int f = 0; f < NF; ++f)
+    kvf[f] = (kj < N) ? global_frag<uint16_t>(KV + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+  f32x16 acc[NDT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    dk_acc[t] = zero16();
-    dv_acc[t] = zero16();
-  }
+  for (int t = 0; t < NDT; ++t) acc[t] = zero16();
   const float c = a.c;
   // Per-lane byte offsets: row reads (A operand, row rho(li), bytes 32f + 16h)
   // and transposing reads (16-lane group g16 gathers rows 4e + h (+2) of a
   // 16-row chunk, columns 32t + 16*(g16&1) + 4*(i16&3) .. +3).
   const int row_off = rho(li) * RS + 16 * h;
   const int tr_off = (4 * (i16 >> 2) + h) * RS + 32 * (g16 & 1) + 8 * (i16 & 3);
+  // P exchange of this pair: [subtile][r/4][lane] x 4 fp32 (16 consecutive bytes per lane).
+  uint8_t* px = smem + 2 * STAGE + pair * PX + 16 * lane;
 
   for (int i = 0; i < nsteps; ++i) {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // step i has landed; every wave is done with step i-1
+    __syncthreads();  // barrier 1: step i has landed; every wave is done with step i-1
     if (i + 1 < nsteps) prefetch(i + 1);
     const int q0 = (qb_start + i % nq) * BQ;
     const uint8_t* st = smem + (i & 1) * STAGE;
+    const float* l2s = reinterpret_cast<const float*>(st + 2 * TILE);
+    const float* dss = l2s + BQ;
+    // Subtile sub (queries q0 + 32 sub ..) is needed unless it is past N or
+    // (causal) every key of the pair follows every query of it.
+    const bool need0 = !CAUSAL || q0 + 31 >= kw0;
+    const bool need1 = q0 + 32 < N && (!CAUSAL || q0 + 63 >= kw0);
+    if (pwave) {
+      // S = Q K^T -> P, for both subtiles; P to LDS and, rounded, to fragments.
+      bf16x8 pf[2][2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int qs0 = q0 + 32 * sub;
-      if (qs0 >= N) break;
-      if (CAUSAL && qs0 + 31 < kw0) continue;  // every key of this wave follows every query
-      const uint8_t* qs = st + sub * 32 * RS;
-      const uint8_t* os = qs + TILE;
-      const float* l2s = reinterpret_cast<const float*>(st + 2 * TILE) + 32 * sub;
-      const float* ds_s = l2s + BQ;
-      // S = Q K^T and dP = dO V^T: rows = queries (rho order), column = key li.
-      f32x16 s = zero16(), dp = zero16();
+      for (int sub = 0; sub < 2; ++sub) {
+        if (!(sub ? need1 : need0)) continue;
+        const int qs0 = q0 + 32 * sub;
+        const uint8_t* qs = st + sub * 32 * RS;
+        f32x16 s = zero16();
 #pragma unroll
-      for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(qs + row_off + 32 * f), kf[f]);
+        for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(qs + row_off + 32 * f), kvf[f]);
+        float p[16];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) mma(dp, *reinterpret_cast<const bf16x8*>(os + row_off + 32 * f), vf[f]);
-      const bool masked = (CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N;
-      float p[16], ds[16];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * sub + 8 * r4 + 4 * h);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 8 * r4 + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds_s + 8 * r4 + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e]));
-          if (masked) {
-            const int qr = qs0 + rho_row(r, h);
-            if (qr >= N || (CAUSAL && kj > qr)) pv = 0.f;
-          }
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
+          for (int e = 0; e < 4; ++e) p[4 * r4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], c, -l4[e]));
         }
+        // Masks: query row >= N, or (causal) key > query.
+        if ((CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N) {
+          const int kd = kj - qs0 - h, nd = N - qs0 - h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int base = rho_row(r, 0);
+            if ((CAUSAL && kd > base) || nd <= base) p[r] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = {p[4 * r4], p[4 * r4 + 1], p[4 * r4 + 2], p[4 * r4 + 3]};
+          *reinterpret_cast<f32x4*>(px + sub * 4096 + r4 * 1024) = v;
+        }
+        pack_frag(pf[sub][0], p);
+        pack_frag(pf[sub][1], p + 8);
       }
-      bf16x8 pf[2], dsf[2];
-      pack_frag(pf[0], p);
-      pack_frag(pf[1], p + 8);
-      pack_frag(dsf[0], ds);
-      pack_frag(dsf[1], ds + 8);
-      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries).
+      __syncthreads();  // barrier 2: P visible to the dS waves
+      // dV^T += dO^T P (contraction over the 32 queries of each subtile).
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
+      for (int sub = 0; sub < 2; ++sub) {
+        if (!(sub ? need1 : need0)) continue;
+        const uint8_t* os = st + TILE + sub * 32 * RS;
 #pragma unroll
-        for (int t = 0; t < NDT; ++t)
-          mma(dv_acc[t], tr_frag(os + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), pf[c2]);
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
+          for (int t = 0; t < NDT; ++t) mma(acc[t], tr_frag(os + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), pf[sub][c2]);
+      }
+    } else {
+      // dP = dO V^T for both subtiles.
+      f32x16 dp[2];
 #pragma unroll
-        for (int t = 0; t < NDT; ++t)
-          mma(dk_acc[t], tr_frag(qs + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), dsf[c2]);
+      for (int sub = 0; sub < 2; ++sub) {
+        dp[sub] = zero16();
+        if (!(sub ? need1 : need0)) continue;
+        const uint8_t* os = st + TILE + sub * 32 * RS;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) mma(dp[sub], *reinterpret_cast<const bf16x8*>(os + row_off + 32 * f), kvf[f]);
+      }
+      __syncthreads();  // barrier 2
+      // dS = P (dP - D), then dK^T += Q^T dS.
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (!(sub ? need1 : need0)) continue;
+        float ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(px + sub * 4096 + r4 * 1024);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * sub + 8 * r4 + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = p4[e] * (dp[sub][4 * r4 + e] - d4[e]);
+        }
+        bf16x8 dsf[2];
+        pack_frag(dsf[0], ds);
+        pack_frag(dsf[1], ds + 8);
+        const uint8_t* qs = st + sub * 32 * RS;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) mma(acc[t], tr_frag(qs + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), dsf[c2]);
+      }
     }
   }
 
   if (kj < N) {
-    uint16_t* dK = static_cast<uint16_t*>(a.dk) + kvoff + (size_t)kj * D;
-    uint16_t* dV = static_cast<uint16_t*>(a.dv) + kvoff + (size_t)kj * D;
+    // P waves hold dV^T, dS waves dK^T (times scale): rows = d, column = key li.
+    uint16_t* out = static_cast<uint16_t*>(pwave ? a.dv : a.dk) + kvoff + (size_t)kj * D;
+    const float mul = pwave ? 1.f : a.scale;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        uint16_t ok[4], ov[4];
+        uint16_t ov[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          to_elem(dk_acc[t][4 * gq + e] * a.scale, ok[e]);
-          to_elem(dv_acc[t][4 * gq + e], ov[e]);
-        }
-        const int col = 32 * t + 8 * gq + 4 * h;
-        *reinterpret_cast<uint2*>(dK + col) = *reinterpret_cast<const uint2*>(ok);
-        *reinterpret_cast<uint2*>(dV + col) = *reinterpret_cast<const uint2*>(ov);
+        for (int e = 0; e < 4; ++e) to_elem(acc[t][4 * gq + e] * mul, ov[e]);
+        *reinterpret_cast<uint2*>(out + 32 * t + 8 * gq + 4 * h) = *reinterpret_cast<const uint2*>(ov);
       }
   }
 }
@@ -358,21 +401,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
 // fp32 starting at the next 256-byte boundary.
 inline size_t bwd_l2_offset_floats(long long rows) { return (size_t)((rows + 63) / 64) * 64; }
 
+// The dQ kernel's instances live in their own translation unit (built with
+// MFMA accumulators in VGPRs, which keeps it within two waves per SIMD).
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int causal, hipStream_t stream);
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NWKV = 4, NWQ = 4;
+  constexpr int NPKV = 4;
   const long long rows = (long long)a.B * a.Hq * a.N;
   float* l2 = a.dsum + bwd_l2_offset_floats(rows);
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a,
                      l2);
-  const int nkb = (a.N + 32 * NWKV - 1) / (32 * NWKV);
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NWKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(64 * NWKV), 0,
+  const int nkb = (a.N + 32 * NPKV - 1) / (32 * NPKV);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NPKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(128 * NPKV), 0,
                      stream, a, (const float*)l2);
-  const int nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NWQ), 0,
-                     stream, a, (const float*)l2);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_bf16(a, l2, D, CAUSAL ? 1 : 0, stream);
 }
 
 }  // namespace fa

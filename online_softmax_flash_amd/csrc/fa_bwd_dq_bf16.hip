@@ -1,0 +1,28 @@
+// dQ kernel instances of the bf16 backward (see fa_bwd_bf16.hpp). This file is
+// compiled with MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the dQ^T
+// accumulator then shares the VGPR file with the scores instead of forcing
+// copies through AGPRs, and the kernel stays within two waves per SIMD.
+#include "fa_bwd_bf16.hpp"
+
+namespace fa {
+
+template <int D, bool CAUSAL>
+static hipError_t dq_bf16(const BwdArgs& a, const float* l2, hipStream_t stream) {
+  constexpr int NWQ = 4;
+  const int nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NWQ), 0,
+                     stream, a, l2);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int causal, hipStream_t stream) {
+  switch (d * 2 + (causal ? 1 : 0)) {
+    case 64 * 2: return dq_bf16<64, false>(a, l2, stream);
+    case 64 * 2 + 1: return dq_bf16<64, true>(a, l2, stream);
+    case 128 * 2: return dq_bf16<128, false>(a, l2, stream);
+    case 128 * 2 + 1: return dq_bf16<128, true>(a, l2, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
