@@ -23,8 +23,10 @@ ARCH = "gfx950"
 
 # No packed fp32 arithmetic (v_pk_*_f32) in device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source additions: the bf16 dQ kernel keeps its MFMA accumulators in VGPRs.
-EXTRA_FLAGS = {"fa_bwd_dq_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions: MFMA accumulators in VGPRs for the bf16 forward and
+# the bf16 dQ kernel (fewer copies between the AGPR and VGPR files).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"fa_bwd_dq_bf16.hip": _VGPR_FORM, "fa_fwd_bf16.hip": _VGPR_FORM}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"]
 
