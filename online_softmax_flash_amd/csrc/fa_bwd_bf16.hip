@@ -13,10 +13,8 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     case 64 * 2 + 1: return launch_bwd_bf16<64, true>(a, stream);
     case 128 * 2: return launch_bwd_bf16<128, false>(a, stream);
     case 128 * 2 + 1: return launch_bwd_bf16<128, true>(a, stream);
-    // d = 256: K, V and both accumulators of 32 keys do not fit one wave's
-    // registers next to the working set; the generic kernels serve it.
-    case 256 * 2: return launch_bwd<uint16_t, 256, 64, false>(a, stream);
-    case 256 * 2 + 1: return launch_bwd<uint16_t, 256, 64, true>(a, stream);
+    case 256 * 2: return launch_bwd_bf16<256, false>(a, stream);
+    case 256 * 2 + 1: return launch_bwd_bf16<256, true>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -407,7 +407,9 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int caus
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NPKV = 4;
+  // Pairs per workgroup: 4 (two waves per SIMD) while a wave's registers allow
+  // it; at d = 256 a wave needs more than half the register file, so 2.
+  constexpr int NPKV = D <= 128 ? 4 : 2;
   const long long rows = (long long)a.B * a.Hq * a.N;
   float* l2 = a.dsum + bwd_l2_offset_floats(rows);
   constexpr int RPB = 256 / (D / 8);

@@ -21,6 +21,8 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int caus
     case 64 * 2 + 1: return dq_bf16<64, true>(a, l2, stream);
     case 128 * 2: return dq_bf16<128, false>(a, l2, stream);
     case 128 * 2 + 1: return dq_bf16<128, true>(a, l2, stream);
+    case 256 * 2: return dq_bf16<256, false>(a, l2, stream);
+    case 256 * 2 + 1: return dq_bf16<256, true>(a, l2, stream);
     default: return hipErrorInvalidValue;
   }
 }
