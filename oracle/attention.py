@@ -20,6 +20,22 @@ The forward is the plain definition, with the whole score matrix of one
    which is the pair (m, l) of fanfani.net section "The backward pass, and where
    the memory saving comes from" folded into one number: P_ij = exp(S_ij - lse_i).
 
+Rectangular problems (Nq queries, Nk keys) align the causal mask to the
+bottom right: query i sees key j iff j <= i + (Nk - Nq), so the last query sees
+every key (the pages only fix the square case; this is the reading that keeps
+the last query of a prefix-extended problem identical). A query row that sees
+no key (possible only when Nq > Nk) has an empty softmax: its output is 0 and
+its lse is -inf.
+
+Partial results over disjoint key ranges (split keys) combine by the same
+rescale step the recurrence applies to each new block (fanfani.net section "A
+pinch of math: making the softmax work in pieces"): each partial (O_s, lse_s)
+enters like one block whose maximum is lse_s and whose exponential sum is 1.
+
+Variable-length batches pack B sequences along the token axis, q [Hq, Tq, d]
+and k, v [Hkv, Tk, d], sequence b owning query rows cu_q[b] .. cu_q[b+1]-1 and
+key rows cu_k[b] .. cu_k[b+1]-1; each sequence is an independent problem.
+
 The backward is derived from that definition by the chain rule (the pages only
 say the score blocks are recomputed from the saved statistics):
 ``dV = P^T dO``, ``dP = dO V^T``, ``D_i = sum_j P_ij dP_ij``,
@@ -39,6 +55,8 @@ __all__ = [
     "attn_fwd_materialised",
     "attn_bwd_group",
     "attn_bwd_analytic",
+    "merge_partials",
+    "attn_fwd_varlen",
 ]
 
 
@@ -54,19 +72,22 @@ def _scores(q_h: np.ndarray, k_h: np.ndarray, scale: float) -> np.ndarray:
     return scale * (q_h @ k_h.T)
 
 
-def _visible(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), n_keys]: key j visible to query rows[r]."""
+def _visible(rows: np.ndarray, n_keys: int, causal: bool, offset: int = 0) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: key j visible to query rows[r] (causal: j <= row + offset)."""
     if not causal:
         return np.ones((rows.shape[0], n_keys), dtype=bool)
-    return np.arange(n_keys)[None, :] <= rows[:, None]
+    return np.arange(n_keys)[None, :] <= rows[:, None] + offset
 
 
 def _softmax_rows(S: np.ndarray):
-    """Max-subtracted softmax of each row; returns (P, m, l)."""
+    """Max-subtracted softmax of each row; returns (P, m, l). A row with no
+    finite score (no visible key) gets P = 0, m = -inf, l = 0."""
     m = S.max(axis=1)
-    E = np.exp(S - m[:, None])
+    seen = np.isfinite(m)
+    E = np.exp(S - np.where(seen, m, 0.0)[:, None])
     l = E.sum(axis=1)
-    return E / l[:, None], m, l
+    P = np.where(seen[:, None], E / np.where(seen, l, 1.0)[:, None], 0.0)
+    return P, m, l
 
 
 def _rows(rows, n: int) -> np.ndarray:
@@ -79,7 +100,7 @@ def attn_probs(q_h, k_h, scale, causal, rows=None) -> np.ndarray:
     k_h = np.asarray(k_h, dtype=np.float64)
     r = _rows(rows, q_h.shape[0])
     S = _scores(q_h[r], k_h, scale)
-    S = np.where(_visible(r, k_h.shape[0], causal), S, -np.inf)
+    S = np.where(_visible(r, k_h.shape[0], causal, k_h.shape[0] - q_h.shape[0]), S, -np.inf)
     P, _, _ = _softmax_rows(S)
     return P
 
@@ -91,16 +112,17 @@ def attn_fwd_head(q_h, k_h, v_h, scale, causal, rows=None):
     v_h = np.asarray(v_h, dtype=np.float64)
     r = _rows(rows, q_h.shape[0])
     S = _scores(q_h[r], k_h, scale)
-    S = np.where(_visible(r, k_h.shape[0], causal), S, -np.inf)
+    S = np.where(_visible(r, k_h.shape[0], causal, k_h.shape[0] - q_h.shape[0]), S, -np.inf)
     P, m, l = _softmax_rows(S)
-    return P @ v_h, m + np.log(l)
+    with np.errstate(divide="ignore"):
+        return P @ v_h, m + np.log(l)
 
 
 def attn_fwd_materialised(q, k, v, scale, causal, rows=None):
     """Forward over all heads.
 
-    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. Returns O [B, Hq, R, d] and
-    lse [B, Hq, R] (float64) for query rows ``rows`` (default all N).
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d]. Returns O [B, Hq, R, d] and
+    lse [B, Hq, R] (float64) for query rows ``rows`` (default all Nq).
     """
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -157,3 +179,54 @@ def attn_bwd_analytic(q, k, v, do, scale, causal):
             hs = slice(g * G, (g + 1) * G)
             dq[b, hs], dk[b, g], dv[b, g] = attn_bwd_group(q[b, hs], k[b, g], v[b, g], do[b, hs], scale, causal)
     return dq, dk, dv
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine partial results over disjoint key ranges.
+
+    o_parts: [S, R, d], each normalised by its own exponential sum;
+    lse_parts: [S, R] natural-log statistics (-inf for a range a row saw no key
+    of). Folds the S partials in order with the recurrence's rescale step:
+    m_new = max(m, lse_s); l = exp(m - m_new) l + exp(lse_s - m_new);
+    o = exp(m - m_new) o + exp(lse_s - m_new) O_s; then O = o / l and
+    lse = m + ln l. Rows with no key in any range get O = 0, lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    S, R = lse_parts.shape
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    o = np.zeros(o_parts.shape[1:])
+    for s_ in range(S):
+        m_new = np.maximum(m, lse_parts[s_])
+        seen = np.isfinite(m_new)
+        base = np.where(seen, m_new, 0.0)
+        alpha = np.where(np.isfinite(m), np.exp(m - base), 0.0)
+        w = np.where(np.isfinite(lse_parts[s_]), np.exp(lse_parts[s_] - base), 0.0)
+        l = alpha * l + w
+        o = alpha[:, None] * o + w[:, None] * o_parts[s_]
+        m = m_new
+    seen = l > 0
+    with np.errstate(divide="ignore"):
+        return np.where(seen[:, None], o / np.where(seen, l, 1.0)[:, None], 0.0), m + np.log(l)
+
+
+def attn_fwd_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """Variable-length batch: q [Hq, Tq, d], k, v [Hkv, Tk, d]; sequence b owns
+    query rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1]. Returns
+    O [Hq, Tq, d] and lse [Hq, Tq] (float64)."""
+    Hq, Tq, _ = q.shape
+    Hkv = k.shape[0]
+    O = np.zeros((Hq, Tq, v.shape[-1]), dtype=np.float64)
+    lse = np.full((Hq, Tq), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        for hq in range(Hq):
+            g = kv_head(hq, Hq, Hkv)
+            if k1 == k0:
+                continue  # no keys: O = 0, lse = -inf
+            O[hq, q0:q1], lse[hq, q0:q1] = attn_fwd_head(q[hq, q0:q1], k[g, k0:k1], v[g, k0:k1], scale, causal)
+    return O, lse

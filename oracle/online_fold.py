@@ -18,6 +18,11 @@ card "The trick: keep a running max, and rebase as you go.":
     m     = m_new
     at the end: O = o / l,  lse = m + ln(l)
 
+With Nq queries and Nk keys the causal mask is aligned to the bottom right
+(key j visible to query i iff j <= i + Nk - Nq). Restricted to a key range
+[key_lo, key_hi) the same loop gives the partial result of that range; a row
+that saw no key of it has O = 0 and lse = -inf.
+
 A block in which a row sees no key leaves that row unchanged (the rescale
 factor is 1 and the block adds nothing); a row that has seen no key yet has
 m = -inf, and its first visible block sets the factor exp(m - m_new) to 0.
@@ -30,24 +35,27 @@ import numpy as np
 __all__ = ["fold_head", "attn_fwd_online_fold"]
 
 
-def fold_head(q_h, k_h, v_h, scale, causal, block_k, rows=None):
-    """One head by the recurrence; returns (O [R, d], lse [R]) in float64."""
+def fold_head(q_h, k_h, v_h, scale, causal, block_k, rows=None, key_lo=0, key_hi=None):
+    """One head by the recurrence over keys [key_lo, key_hi) (default all);
+    returns (O [R, d], lse [R]) in float64."""
     q_h = np.asarray(q_h, dtype=np.float64)
     k_h = np.asarray(k_h, dtype=np.float64)
     v_h = np.asarray(v_h, dtype=np.float64)
     n_keys = k_h.shape[0]
+    offset = n_keys - q_h.shape[0]
+    key_hi = n_keys if key_hi is None else key_hi
     qi = np.arange(q_h.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     qr = q_h[qi]
     R = qr.shape[0]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     o = np.zeros((R, v_h.shape[1]))
-    for j0 in range(0, n_keys, block_k):
-        j1 = min(j0 + block_k, n_keys)
+    for j0 in range(key_lo, key_hi, block_k):
+        j1 = min(j0 + block_k, key_hi)
         s = scale * (qr @ k_h[j0:j1].T)
         if causal:
             keys = np.arange(j0, j1)
-            s = np.where(keys[None, :] <= qi[:, None], s, -np.inf)
+            s = np.where(keys[None, :] <= qi[:, None] + offset, s, -np.inf)
         m_blk = s.max(axis=1)
         m_new = np.maximum(m, m_blk)
         seen = np.isfinite(m_new)
@@ -58,7 +66,9 @@ def fold_head(q_h, k_h, v_h, scale, causal, block_k, rows=None):
         l = alpha * l + p.sum(axis=1)
         o = alpha[:, None] * o + p @ v_h[j0:j1]
         m = m_new
-    return o / l[:, None], m + np.log(l)
+    seen = l > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(seen[:, None], o / l[:, None], 0.0), m + np.log(l)
 
 
 def attn_fwd_online_fold(q, k, v, scale, causal, block_k, rows=None):

@@ -38,6 +38,8 @@ def make_ns(att, fold):
         kv_head=att.kv_head,
         attn_fwd_online_fold=fold.attn_fwd_online_fold,
         fold_head=fold.fold_head,
+        merge_partials=att.merge_partials,
+        attn_fwd_varlen=att.attn_fwd_varlen,
     )
 
 
@@ -177,11 +179,18 @@ def pin_special_rows(ns):
 
 
 def _brute_head(q, k, v, scale, causal):
-    """Pure-Python loops from the definition (scores, mask, softmax, weighted sum)."""
+    """Pure-Python loops from the definition (scores, mask, softmax, weighted
+    sum). With len(q) queries and len(k) keys the causal mask is aligned to the
+    bottom right (key j visible to query i iff j <= i + len(k) - len(q)); a
+    query that sees no key gets output 0 and lse -inf."""
     n, d = len(q), len(q[0])
     O, L = [], []
     for i in range(n):
-        keys = [j for j in range(len(k)) if (not causal or j <= i)]
+        keys = [j for j in range(len(k)) if (not causal or j <= i + len(k) - n)]
+        if not keys:
+            O.append([0.0] * len(v[0]))
+            L.append(-math.inf)
+            continue
         s = [scale * sum(q[i][c] * k[j][c] for c in range(d)) for j in keys]
         mx = max(s)
         w = [math.exp(x - mx) for x in s]
@@ -318,6 +327,134 @@ def pin_bwd_qzero_causal(ns):
     _close(dv[0, 0], expect, 1e-12, "Q=0 causal dV closed form")
 
 
+
+# ---------------------------------------------------------------------------
+# Rectangular problems, split keys, variable-length batches
+# ---------------------------------------------------------------------------
+
+def _close_inf(a, b, tol, what):
+    """As _close, with -inf required at exactly the same places."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    ia, ib = np.isneginf(a), np.isneginf(b)
+    assert np.array_equal(ia, ib), f"{what}: -inf at different places"
+    _close(np.where(ia, 0.0, a), np.where(ib, 0.0, b), tol, what)
+
+
+def pin_rectangular_causal(ns):
+    """Nq != Nk: brute force (bottom-right mask), the single-query closed case
+    (the last query sees every key, so causal equals full attention), the
+    prefix-extension identity (the rectangular problem is the last Nq rows of
+    the square one whose first Nk - Nq queries are arbitrary), and rows that
+    see no key (Nq > Nk): output exactly 0, lse exactly -inf."""
+    sc = 0.45
+    for Nq, Nk in [(1, 9), (3, 11), (5, 5), (7, 4)]:
+        q = _rand((Nq, 3), 100 + Nq)
+        k = _rand((Nk, 3), 200 + Nk)
+        v = _rand((Nk, 2), 300 + Nk)
+        for causal in (False, True):
+            Ob, Lb = _brute_head(q.tolist(), k.tolist(), v.tolist(), sc, causal)
+            O1, l1 = ns.attn_fwd_head(q, k, v, sc, causal)
+            O2, l2 = ns.fold_head(q, k, v, sc, causal, 3)
+            for O, l, tag in ((O1, l1, "definition"), (O2, l2, "fold")):
+                _close(O, Ob, TOL, f"{tag} O Nq={Nq} Nk={Nk} causal={causal}")
+                _close_inf(l, Lb, TOL, f"{tag} lse Nq={Nq} Nk={Nk} causal={causal}")
+    q = _rand((1, 8), 7)
+    k = _rand((40, 8), 8)
+    v = _rand((40, 8), 9)
+    Oc, lc = ns.attn_fwd_head(q, k, v, sc, True)
+    On, ln = ns.attn_fwd_head(q, k, v, sc, False)
+    _close(Oc, On, TOL, "one query: causal == full")
+    _close(lc, ln, TOL, "one query: causal == full (lse)")
+    Nq, Nk = 6, 17
+    q = _rand((Nq, 5), 21)
+    k = _rand((Nk, 5), 22)
+    v = _rand((Nk, 4), 23)
+    qfull = np.concatenate([_rand((Nk - Nq, 5), 24), q])
+    Os, ls = ns.attn_fwd_head(qfull, k, v, sc, True)
+    for O, l, tag in (ns.attn_fwd_head(q, k, v, sc, True) + ("definition",),
+                      ns.fold_head(q, k, v, sc, True, 4) + ("fold",)):
+        _close(O, Os[Nk - Nq:], TOL, f"{tag}: prefix extension O")
+        _close(l, ls[Nk - Nq:], TOL, f"{tag}: prefix extension lse")
+    q = _rand((9, 4), 31)
+    k = _rand((3, 4), 32)
+    v = _rand((3, 4), 33)
+    for O, l, tag in (ns.attn_fwd_head(q, k, v, sc, True) + ("definition",),
+                      ns.fold_head(q, k, v, sc, True, 2) + ("fold",)):
+        assert np.all(O[:6] == 0.0) and np.all(np.isneginf(l[:6])), f"{tag}: rows without keys"
+        assert np.all(np.isfinite(l[6:])), f"{tag}: rows with keys"
+
+
+def pin_merge_partials(ns):
+    """Split keys: partial results over disjoint key ranges (one of them empty,
+    one ragged) merged by the rescale step equal the full softmax; the order of
+    the partials does not matter; one partial merges to itself; two partials
+    with equal lse and outputs a, b give (a + b) / 2 and lse + ln 2 (closed
+    form); ranges a row sees no key of (lse -inf) add nothing, and a row with
+    no key anywhere gets 0 and -inf."""
+    sc = 0.3
+    Nq, Nk, d = 6, 23, 5
+    q = _rand((Nq, d), 41)
+    k = _rand((Nk, d), 42)
+    v = _rand((Nk, d), 43)
+    bounds = [0, 5, 5, 12, 23]
+    for causal in (False, True):
+        parts = [ns.fold_head(q, k, v, sc, causal, 4, key_lo=a, key_hi=b) for a, b in zip(bounds, bounds[1:])]
+        o_parts = np.stack([p[0] for p in parts])
+        l_parts = np.stack([p[1] for p in parts])
+        Oref, lref = ns.attn_fwd_head(q, k, v, sc, causal)
+        O, l = ns.merge_partials(o_parts, l_parts)
+        _close(O, Oref, TOL, f"merge == full causal={causal}")
+        _close(l, lref, TOL, f"merge lse == full causal={causal}")
+        perm = [3, 1, 0, 2]
+        O2, l2 = ns.merge_partials(o_parts[perm], l_parts[perm])
+        _close(O2, Oref, TOL, f"merge order causal={causal}")
+        _close(l2, lref, TOL, f"merge order lse causal={causal}")
+    O1, l1 = ns.merge_partials(o_parts[2:3], l_parts[2:3])
+    _close(O1, o_parts[2], TOL, "single partial O")
+    _close(l1, l_parts[2], TOL, "single partial lse")
+    a = _rand((3, 4), 44)
+    b = _rand((3, 4), 45)
+    lse = np.array([0.3, -2.0, 5.0])
+    O, l = ns.merge_partials(np.stack([a, b]), np.stack([lse, lse]))
+    _close(O, (a + b) / 2, TOL, "equal-lse closed form O")
+    _close(l, lse + math.log(2.0), TOL, "equal-lse closed form lse")
+    lp = np.array([[-np.inf, 1.0], [-np.inf, -np.inf]])
+    op = np.stack([np.zeros((2, 4)), np.zeros((2, 4))])
+    op[0, 1] = 7.0
+    O, l = ns.merge_partials(op, lp)
+    assert np.all(O[0] == 0.0) and np.isneginf(l[0]), "no key anywhere"
+    _close(O[1], op[0, 1], TOL, "empty ranges add nothing")
+    _close(l[1], 1.0, TOL, "empty ranges add nothing (lse)")
+
+
+def pin_varlen(ns):
+    """Variable-length batch (sequences packed along the token axis, GQA):
+    every sequence against brute force on its own rows, including a sequence
+    with no queries, one with no keys (outputs 0, lse -inf) and a rectangular
+    causal one."""
+    sc = 0.5
+    cu_q = [0, 3, 3, 8, 10]
+    cu_k = [0, 5, 9, 9, 16]
+    Hq, Hkv, d = 4, 2, 3
+    q = _rand((Hq, cu_q[-1], d), 51)
+    k = _rand((Hkv, cu_k[-1], d), 52)
+    v = _rand((Hkv, cu_k[-1], d), 53)
+    for causal in (False, True):
+        O, l = ns.attn_fwd_varlen(q, k, v, cu_q, cu_k, sc, causal)
+        for b in range(len(cu_q) - 1):
+            q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            for hq in range(Hq):
+                g = hq // 2
+                if k1 == k0:
+                    assert np.all(O[hq, q0:q1] == 0.0) and np.all(np.isneginf(l[hq, q0:q1])), "no keys"
+                    continue
+                if q1 == q0:
+                    continue
+                Ob, Lb = _brute_head(q[hq, q0:q1].tolist(), k[g, k0:k1].tolist(), v[g, k0:k1].tolist(), sc, causal)
+                _close(O[hq, q0:q1], Ob, TOL, f"varlen O seq={b} hq={hq} causal={causal}")
+                _close_inf(l[hq, q0:q1], Lb, TOL, f"varlen lse seq={b} hq={hq} causal={causal}")
+
 FWD_PINS = [
     pin_fold_equals_definition,
     pin_rows_sum_to_one,
@@ -327,6 +464,9 @@ FWD_PINS = [
     pin_brute_force,
     pin_golden,
     pin_gqa_is_repeated_kv,
+    pin_rectangular_causal,
+    pin_merge_partials,
+    pin_varlen,
 ]
 BWD_PINS = [
     pin_bwd_finite_difference,

@@ -25,7 +25,7 @@ MUTATIONS = [
     ("scores_no_scale", ATT, "return scale * (q_h @ k_h.T)", "return (q_h @ k_h.T)"),
     ("mask_reversed", ATT, "<= rows[:, None]", ">= rows[:, None]"),
     ("mask_off_by_one", ATT, "<= rows[:, None]", "< rows[:, None] + 2"),
-    ("softmax_no_max", ATT, "E = np.exp(S - m[:, None])", "E = np.exp(S)"),
+    ("softmax_no_max", ATT, "E = np.exp(S - np.where(seen, m, 0.0)[:, None])", "E = np.exp(S)"),
     ("softmax_wrong_axis", ATT, "l = E.sum(axis=1)", "l = E.sum(axis=0)"),
     ("lse_dropped_log", ATT, "return P @ v_h, m + np.log(l)", "return P @ v_h, m"),
     ("pv_transposed", ATT, "return P @ v_h, m + np.log(l)", "return P.T @ v_h, m + np.log(l)"),
@@ -39,8 +39,21 @@ MUTATIONS = [
     ("fold_no_rescale_l", FOLD, "l = alpha * l + p.sum(axis=1)", "l = l + p.sum(axis=1)"),
     ("fold_no_rescale_o", FOLD, "o = alpha[:, None] * o + p @ v_h[j0:j1]", "o = o + p @ v_h[j0:j1]"),
     ("fold_keeps_block_max", FOLD, "        m = m_new\n", "        m = m_blk\n"),
-    ("fold_no_final_divide", FOLD, "return o / l[:, None], m + np.log(l)", "return o, m + np.log(l)"),
+    ("fold_no_final_divide", FOLD, "np.where(seen[:, None], o / l[:, None], 0.0)", "np.where(seen[:, None], o, 0.0)"),
     ("fold_mask_strict", FOLD, "keys[None, :] <= qi[:, None]", "keys[None, :] < qi[:, None]"),
+    ("offset_sign", ATT, "<= rows[:, None] + offset", "<= rows[:, None] - offset"),
+    ("offset_top_left", ATT, "causal, k_h.shape[0] - q_h.shape[0]), S, -np.inf)\n    P, m, l",
+     "causal, 0), S, -np.inf)\n    P, m, l"),
+    ("empty_row_uniform", ATT, "P = np.where(seen[:, None], E / np.where(seen, l, 1.0)[:, None], 0.0)",
+     "P = np.where(seen[:, None], E / np.where(seen, l, 1.0)[:, None], 1.0 / S.shape[1])"),
+    ("merge_no_rescale", ATT, "l = alpha * l + w", "l = l + w"),
+    ("merge_unweighted", ATT, "w = np.where(np.isfinite(lse_parts[s_]), np.exp(lse_parts[s_] - base), 0.0)",
+     "w = np.where(np.isfinite(lse_parts[s_]), 1.0, 0.0)"),
+    ("merge_no_divide", ATT, "o / np.where(seen, l, 1.0)[:, None], 0.0), m + np.log(l)",
+     "o, 0.0), m + np.log(l)"),
+    ("varlen_key_rows", ATT, "k[g, k0:k1], v[g, k0:k1]", "k[g, q0:q1], v[g, q0:q1]"),
+    ("fold_offset_dropped", FOLD, "<= qi[:, None] + offset", "<= qi[:, None]"),
+    ("fold_range_from_zero", FOLD, "range(key_lo, key_hi, block_k)", "range(0, key_hi, block_k)"),
     ("fold_wrong_scale", FOLD, "s = scale * (qr @ k_h[j0:j1].T)", "s = scale * scale * (qr @ k_h[j0:j1].T)"),
 ]
 
