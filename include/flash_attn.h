@@ -76,7 +76,7 @@ typedef enum {
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   FA_ERR_SCALE = 5,       /* scale is not finite or is negative */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  FA_ERR_WORKSPACE = 7    /* backward workspace NULL or smaller than flash_attn_bwd_workspace_bytes */
+  FA_ERR_WORKSPACE = 7    /* a required workspace is NULL or smaller than its *_workspace_bytes */
 } fa_status;
 
 /*
@@ -95,6 +95,61 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 /* Forward, fp32 check mode: as flash_attn_fwd with fp32 q, k, v, o. */
 int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * General forward, bf16 storage: rectangular problems, split keys, and
+ * variable-length batches. Same operation as flash_attn_fwd per (sequence,
+ * query head), with these differences:
+ *   - Nq queries and Nk keys per sequence; the causal mask is aligned to the
+ *     bottom right: query i sees key j iff j <= i + Nk - Nq, so the last query
+ *     sees every key (with Nq == Nk this is flash_attn_fwd's mask). A query
+ *     that sees no key (causal with Nq > Nk) gets O = 0 and lse = -inf.
+ *   - Split keys (decoding: few queries, a long key/value cache): the keys of
+ *     each sequence are cut into num_splits ranges, each range gives a
+ *     partial result (o/l in fp32 and its lse) in the workspace, and a second
+ *     kernel merges them with the online softmax's rescale step (fanfani.net
+ *     "FlashAttention", section "A pinch of math: making the softmax work in
+ *     pieces": a partial enters like one block whose maximum is its lse and
+ *     whose exponential sum is 1). The result equals the unsplit one up to
+ *     fp32 rounding order.
+ *   - The G = Hq/Hkv query heads of a K/V head share each staged K/V block.
+ *
+ * flash_attn_fwd_kv: uniform lengths.
+ *   q, o [B,Hq,Nq,d], k, v [B,Hkv,Nk,d] (bf16 bits), lse [B,Hq,Nq] fp32.
+ * flash_attn_fwd_varlen: B sequences packed along the token axis.
+ *   q, o [Hq,Tq,d], k, v [Hkv,Tk,d] (bf16 bits), lse [Hq,Tq] fp32;
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B+1], non-decreasing, from 0 to
+ *   Tq (resp. Tk): sequence b owns query tokens cu_seqlens_q[b] ..
+ *   cu_seqlens_q[b+1]-1 and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+ *   max_seqlen_q / max_seqlen_k: upper bounds of the per-sequence lengths (they
+ *   size the launch). Offsets are clamped into [0, T] on the device, so any
+ *   contents keep every access in bounds, but query tokens beyond
+ *   max_seqlen_q in a sequence and tokens outside every sequence are left
+ *   unspecified.
+ * num_splits: 1 = no split; 0 = the library's choice
+ *   (flash_attn_fwd_kv_num_splits); at most 256.
+ * workspace: caller-owned device buffer of flash_attn_fwd_kv_workspace_bytes(
+ *   rows, d, splits) bytes, rows = B*Hq*Nq (uniform) or Hq*Tq (varlen), with
+ *   the split count actually used; NULL is allowed when that is 1. Contents on
+ *   entry ignored, on return unspecified.
+ * Errors as flash_attn_fwd; FA_ERR_SHAPE also for num_splits outside
+ * [0, 256], FA_ERR_WORKSPACE for a missing or short workspace.
+ */
+int flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                          int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count the library picks for num_splits = 0 (Nq, Nk: the largest
+ * sequence lengths); 0 for invalid sizes. */
+int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/* Workspace bytes of the general forward for `rows` query rows and
+ * `num_splits` splits (0 when num_splits == 1; 0 for invalid sizes). */
+size_t flash_attn_fwd_kv_workspace_bytes(long long rows, int d, int num_splits);
 
 /*
  * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these

@@ -23,7 +23,13 @@ __all__ = [
     "flash_attn_bwd_f32",
     "flash_attn_bwd_workspace_bytes",
     "flash_attn_status_str",
+    "flash_attn_fwd_kv",
+    "flash_attn_fwd_varlen",
+    "flash_attn_fwd_kv_num_splits",
+    "flash_attn_fwd_kv_workspace_bytes",
     "attention_forward",
+    "attention_forward_kv",
+    "attention_forward_varlen",
     "attention_backward",
 ]
 
@@ -63,6 +69,15 @@ def load_library():
     lib.flash_attn_bwd_f32.restype = I
     lib.flash_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.flash_attn_bwd_workspace_bytes.restype = Z
+    L = ctypes.c_longlong
+    lib.flash_attn_fwd_kv.argtypes = [P] * 5 + [I] * 6 + [F, I, I, P, Z, P]
+    lib.flash_attn_fwd_kv.restype = I
+    lib.flash_attn_fwd_varlen.argtypes = [P] * 7 + [I] * 8 + [F, I, I, P, Z, P]
+    lib.flash_attn_fwd_varlen.restype = I
+    lib.flash_attn_fwd_kv_num_splits.argtypes = [I] * 6
+    lib.flash_attn_fwd_kv_num_splits.restype = I
+    lib.flash_attn_fwd_kv_workspace_bytes.argtypes = [L, I, I]
+    lib.flash_attn_fwd_kv_workspace_bytes.restype = Z
     lib.flash_attn_status_str.argtypes = [I]
     lib.flash_attn_status_str.restype = ctypes.c_char_p
     _LIB = lib
@@ -184,3 +199,94 @@ def attention_backward(q, k, v, o, lse, dout, scale, causal, stream=None):
     fn = flash_attn_bwd if q.dtype == torch.bfloat16 else flash_attn_bwd_f32
     fn(q, k, v, o, lse, dout, dq, dk, dv, ws, scale, causal, stream)
     return dq, dk, dv
+
+
+def flash_attn_fwd_kv_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return int(load_library().flash_attn_fwd_kv_num_splits(int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d)))
+
+
+def flash_attn_fwd_kv_workspace_bytes(rows, d, num_splits) -> int:
+    return int(load_library().flash_attn_fwd_kv_workspace_bytes(int(rows), int(d), int(num_splits)))
+
+
+def _ws_size(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def flash_attn_fwd_kv(q, k, v, o, lse, scale, causal, num_splits=1, workspace=None, stream=None):
+    """bf16 forward with Nq queries and Nk keys (bottom-right causal), optionally
+    split over keys: q, o [B,Hq,Nq,d], k, v [B,Hkv,Nk,d], lse [B,Hq,Nq] fp32."""
+    import torch
+    _check(q, k, v, o, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    if workspace is not None:
+        _check(workspace)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = (int(x) for x in q.shape)
+    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    st = load_library().flash_attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                          float(scale), int(bool(causal)), int(num_splits), _ptr(workspace),
+                                          _ws_size(workspace), _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_fwd_kv", st)
+
+
+def flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal,
+                          num_splits=1, workspace=None, stream=None):
+    """bf16 forward over a variable-length batch: q, o [Hq,Tq,d], k, v [Hkv,Tk,d],
+    lse [Hq,Tq] fp32, cu_seqlens_* int32 [B+1] on the GPU."""
+    import torch
+    _check(q, k, v, o, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    _check(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    if workspace is not None:
+        _check(workspace)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [Hq, Tq, d] and k, v [Hkv, Tk, d]")
+    Hq, Tq, d = (int(x) for x in q.shape)
+    Hkv, Tk = int(k.shape[0]), int(k.shape[1])
+    B = int(cu_seqlens_q.numel()) - 1
+    st = load_library().flash_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                              _ptr(cu_seqlens_k), B, Hq, Hkv, Tq, Tk, int(max_seqlen_q),
+                                              int(max_seqlen_k), d, float(scale), int(bool(causal)),
+                                              int(num_splits), _ptr(workspace), _ws_size(workspace),
+                                              _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_fwd_varlen", st)
+
+
+def _kv_workspace(rows, d, splits, device):
+    import torch
+    n = flash_attn_fwd_kv_workspace_bytes(rows, d, splits)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attention_forward_kv(q, k, v, scale, causal, num_splits=0, stream=None):
+    """Allocate o, lse and the workspace with torch and run flash_attn_fwd_kv
+    (num_splits=0: the library's choice)."""
+    import torch
+    B, Hq, Nq, d = (int(x) for x in q.shape)
+    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    splits = num_splits or flash_attn_fwd_kv_num_splits(B, Hq, Hkv, Nq, Nk, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ws = _kv_workspace(B * Hq * Nq, d, splits, q.device)
+    flash_attn_fwd_kv(q, k, v, o, lse, scale, causal, splits, ws, stream)
+    return o, lse
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal,
+                             num_splits=0, stream=None):
+    """Allocate o, lse and the workspace with torch and run flash_attn_fwd_varlen."""
+    import torch
+    Hq, Tq, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[0])
+    B = int(cu_seqlens_q.numel()) - 1
+    splits = num_splits or flash_attn_fwd_kv_num_splits(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    ws = _kv_workspace(Hq * Tq, d, splits, q.device)
+    flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal,
+                          splits, ws, stream)
+    return o, lse

@@ -74,6 +74,84 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+
+// Split count for the general forward: one unless the (batch, K/V head, row
+// block) workgroups are too few to fill the chip; then enough splits for about
+// four workgroups per compute unit, each split at least 256 keys.
+int kv_splits_auto(int B, int Hq, int Hkv, int max_nq, int max_nk) {
+  const long long G = Hq / Hkv;
+  const long long rows = (long long)max_nq * G;
+  const long long bm = rows <= 32 ? 32 : 128;
+  const long long wgs = (long long)B * Hkv * ((rows + bm - 1) / bm);
+  const long long target = 4 * 256;
+  if (wgs >= target / 2 || max_nk <= 512) return 1;
+  long long s = (target + wgs - 1) / wgs;
+  s = s < (max_nk + 255) / 256 ? s : (max_nk + 255) / 256;
+  s = s < 256 ? s : 256;
+  return (int)(s < 1 ? 1 : s);
+}
+
+size_t kv_workspace(long long rows, int d, int splits) {
+  if (splits <= 1) return 0;
+  const size_t po = (size_t)splits * rows * d * 4;
+  const size_t pl = (size_t)splits * rows * 4;
+  return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
+}
+
+int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q, const int* cu_k,
+              int B, int Hq, int Hkv, int Nq, int Nk, int max_nq, int max_nk, int d, float scale, int causal,
+              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse};
+  int st = check_ptrs(ptrs, 5);
+  if (st != FA_OK) return st;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Nq <= 0 || Nk <= 0 || max_nq <= 0 || max_nk <= 0)
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (num_splits < 0) return FA_ERR_SHAPE;
+  const long long rows = cu_q ? (long long)Hq * Nq : (long long)B * Hq * Nq;
+  const long long krows = cu_q ? (long long)Hkv * Nk : (long long)B * Hkv * Nk;
+  if (rows * d > ((long long)1 << 40) || krows * d > ((long long)1 << 40)) return FA_ERR_SHAPE;
+  const long long G = Hq / Hkv;
+  const long long nrb = ((long long)max_nq * G + 31) / 32;
+  if ((long long)max_nq * G > 0x7fffffffLL || nrb * 256 > 0x7fffffffLL || Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;
+  st = check_scale(scale);
+  if (st != FA_OK) return st;
+  const int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk) : num_splits;
+  if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
+  if (splits > 1) {
+    if (workspace == nullptr) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if (workspace_bytes < kv_workspace(rows, d, splits)) return FA_ERR_WORKSPACE;
+  }
+  fa::KvArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.max_nq = max_nq;
+  a.max_nk = max_nk;
+  a.num_splits = splits;
+  a.split_keys = (((max_nk + splits - 1) / splits) + 63) / 64 * 64;
+  a.rows = rows;
+  a.c = scale * kLog2e;
+  if (splits > 1) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + (((size_t)splits * rows * d * 4 + 255) & ~(size_t)255));
+  }
+  const hipError_t e = fa::fwd_kv_bf16(a, d, causal, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +187,33 @@ int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const flo
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
   return bwd_common(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
                     stream);
+}
+
+int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Nq <= 0 || Nk <= 0) return 0;
+  if (d != 64 && d != 128 && d != 256) return 0;
+  return kv_splits_auto(B, Hq, Hkv, Nq, Nk);
+}
+
+size_t flash_attn_fwd_kv_workspace_bytes(long long rows, int d, int num_splits) {
+  if (rows <= 0 || (d != 64 && d != 128 && d != 256) || num_splits < 1 || num_splits > 256) return 0;
+  return kv_workspace(rows, d, num_splits);
+}
+
+int flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return kv_common(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, Nq, Nk, d, scale, causal, num_splits,
+                   workspace, workspace_bytes, stream);
+}
+
+int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                          int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERR_NULL;
+  return kv_common(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, Tq, Tk, max_seqlen_q, max_seqlen_k, d,
+                   scale, causal, num_splits, workspace, workspace_bytes, stream);
 }
 
 const char* flash_attn_status_str(int status) {

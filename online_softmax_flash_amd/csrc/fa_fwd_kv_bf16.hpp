@@ -1,0 +1,344 @@
+// General forward, bf16 storage: rectangular problems (Nq queries, Nk keys,
+// causal mask aligned to the bottom right), variable-length batches packed
+// along the token axis, and split keys with a combine step.
+//
+// Per query row the kernel runs the same online-softmax recurrence as the
+// square forward (fanfani.net "FlashAttention", section "A pinch of math:
+// making the softmax work in pieces"), over the keys of one split only. With
+// one split it writes O and lse directly. With several, each split writes its
+// partial result (o / l in fp32, lse = m + ln l) and fwd_combine_kernel merges
+// them with the recurrence's own rescale step: each partial enters like one
+// block whose maximum is its lse and whose exponential sum is 1. That is the
+// step that serves decoding (few queries, a long key/value cache: the work is
+// reading K and V, section "What changed in practice" on the pages' serving
+// remarks), where one (batch, K/V head) alone cannot fill the chip.
+//
+// Rows. The G query heads that share a K/V head are packed into the rows of
+// one workgroup: packed row r of (batch b, K/V head hkv) is query position
+// r / G of query head hkv*G + r % G. A decode step (Nq = 1) thus fills G rows
+// of a tile instead of one, and every K/V block staged in LDS serves all of
+// them. Data movement is that of the square bf16 forward (fa_fwd_bf16.hpp):
+// K and V blocks of 64 keys direct to LDS, double-buffered, padded rows, V
+// read with transposing reads; Q rows in registers as B operands.
+//
+// Conventions: query i of a sequence with nq queries and nk keys sees key j
+// iff j <= i + nk - nq (causal) and j < nk; a row that sees no key gets O = 0
+// and lse = -inf.
+#pragma once
+
+#include "fa_fwd_bf16.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// Direct global->LDS copy of rows [0, BN) of a row-major bf16 [*, D] matrix
+// into BN rows of ROWB bytes, in the slot order of BlockDma (wave-instruction
+// n fills 16-byte slots 64n .. 64n+63; padding slots are skipped), but with
+// each lane's source offset recomputed at every call instead of held in
+// registers: a workgroup of one wave issues all the block's instructions, and
+// keeping their offsets would cost two registers per instruction.
+template <int D, int BN, int ROWB, int NW>
+struct LeanDma {
+  static constexpr int SPR = ROWB / 16;
+  static constexpr int CPR = 2 * D / 16;
+  static constexpr int NINSTR = (BN * SPR + 63) / 64;
+  template <bool FULL>
+  __device__ __forceinline__ static void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) {
+    asm volatile("" : "+v"(lane));  // recompute below on every call
+#pragma unroll
+    for (int n0 = 0; n0 < NINSTR; n0 += NW) {
+      const int n = n0 + wave;
+      if (n0 + NW <= NINSTR || n < NINSTR) {  // wave-uniform
+        const int slot = n * 64 + lane;
+        const int r = slot / SPR, c = slot - r * SPR;
+        if (c < CPR && r < BN) {
+          const int rr = (!FULL && r >= valid) ? valid - 1 : r;
+          __builtin_amdgcn_global_load_lds(g + rr * D + c * 8, (lds_void_t*)(lds + n * 1024), 16, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
+  constexpr int BN = 64;
+  using C = Bf16FwdCfg<D, BN, NW>;
+  constexpr int BM = C::BM;
+  constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
+  constexpr float TAU = 8.0f;
+  constexpr int STAGE = C::KBYTES + C::VBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int split = blockIdx.x % a.num_splits;
+  const int rb = blockIdx.x / a.num_splits;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+
+  // Sequence b: query rows qs .. qs+nq-1, key rows ks .. ks+nk-1 of each head.
+  int qs = 0, nq = a.Nq, ks = 0, nk = a.Nk;
+  long long q_bs = (long long)a.Hq * a.Nq, q_hs = a.Nq, k_bs = (long long)a.Hkv * a.Nk, k_hs = a.Nk;
+  if (a.cu_q != nullptr) {
+    // Offsets are clamped into [0, total] and lengths to the grid's maximum,
+    // so that any offsets keep every access in bounds.
+    qs = min(max(a.cu_q[b], 0), a.Nq);
+    nq = min(min(max(a.cu_q[b + 1], qs), a.Nq) - qs, a.max_nq);
+    ks = min(max(a.cu_k[b], 0), a.Nk);
+    nk = min(max(a.cu_k[b + 1], ks), a.Nk) - ks;
+    q_bs = 0;
+    k_bs = 0;
+  }
+  const int nrows = nq * G;
+  const int r0 = rb * BM;
+  if (r0 >= nrows) return;  // uniform over the workgroup: no barrier reached yet
+
+  // This lane's packed row: query i of head hkv*G + g.
+  const int r = r0 + wave * 32 + li;
+  const bool row_ok = r < nrows;
+  const int i = r / G, hq = hkv * G + r % G;
+  const long long row = (long long)b * q_bs + (long long)hq * q_hs + qs + i;  // also the lse / output row index
+  const int off = nk - nq;  // causal: key j visible iff j <= i + off
+
+  // Keys of this split, cut at the last key any row of the workgroup sees.
+  const int i_last = min(nrows - 1, r0 + BM - 1) / G;
+  int kend = min(nk, (split + 1) * a.split_keys);
+  if (CAUSAL) kend = min(kend, i_last + off + 1);
+  const int kbeg = split * a.split_keys;
+  const int kb0 = kbeg / BN;
+  const int kb_end = kend > kbeg ? (kend + BN - 1) / BN : kb0;
+  // Blocks below kb_full need no mask: every key < kend and (causal) visible
+  // to the workgroup's first row.
+  const int i_first = r0 / G;
+  int kfull = kend;
+  if (CAUSAL) kfull = min(kfull, i_first + off + 1);
+  const int kb_full = max(kb0, kfull / BN);
+  // This wave's last row: blocks past its limit are skipped (causal).
+  const int wlast = min(nrows - 1, r0 + wave * 32 + 31);
+  const int wave_kmax = CAUSAL ? (wlast / G + off) : (kend - 1);
+
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + ((long long)b * k_bs + (long long)hkv * k_hs + ks) * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + ((long long)b * k_bs + (long long)hkv * k_hs + ks) * D;
+
+  using KDma = LeanDma<D, BN, C::KROW, NW>;
+  using VDma = LeanDma<D, BN, C::VROW, NW>;
+  auto prefetch = [&](int kb) {
+    uint8_t* st = smem + (kb & 1) * STAGE;
+    const uint16_t* kg = K + (size_t)kb * BN * D;
+    const uint16_t* vg = V + (size_t)kb * BN * D;
+    const int valid = kend - kb * BN;
+    if (valid >= BN) {
+      KDma::template issue<true>(st, kg, BN, wave, lane);
+      VDma::template issue<true>(st + C::KBYTES, vg, BN, wave, lane);
+    } else {
+      KDma::template issue<false>(st, kg, valid, wave, lane);
+      VDma::template issue<false>(st + C::KBYTES, vg, valid, wave, lane);
+    }
+  };
+  if (kb0 < kb_end) prefetch(kb0);
+
+  bf16x8 qf[NF];
+  const uint16_t* Qr = static_cast<const uint16_t*>(a.q) + row * D;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) qf[f] = row_ok ? global_frag<uint16_t>(Qr + 16 * f + 8 * h) : zero_frag<bf16x8>();
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = zero16();
+  float m_run = -INFINITY;
+  float l_bf = 0.f, l_32 = 0.f;
+  const float c = a.c;
+  const int k_off = sigma(li) * C::KROW + 16 * h;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int v_off = C::KBYTES + (8 * h + (i16 >> 2)) * C::VROW + 2 * (16 * (g16 & 1) + 4 * (i16 & 3));
+  const int klim = CAUSAL ? min(kend - 1, i + off) : kend - 1;  // last key this row sees
+
+  auto block = [&](int kb, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = kb * BN;
+    if (CAUSAL && k0 > wave_kmax) return;
+    const uint8_t* st = smem + (kb & 1) * STAGE;
+    f32x16 s[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      s[kt] = zero16();
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        mma(s[kt], *reinterpret_cast<const bf16x8*>(st + k_off + 32 * kt * C::KROW + 32 * f), qf[f]);
+    }
+    bool keep[NKT][16];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          keep[kt][e] = k0 + 32 * kt + sigma_row(e, h) <= klim;
+          if (!keep[kt][e]) s[kt][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    if (__any(mxc > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mxc);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_bf *= alpha;
+      l_32 *= alpha;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+    }
+    const float base = (m_run == -INFINITY) ? 0.f : m_run;
+    float p32[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], c, -base));
+        if constexpr (MASKED) p = keep[kt][e] ? p : 0.f;
+        s[kt][e] = p;
+        p32[e & 1] += p;
+      }
+    l_32 += p32[0] + p32[1];
+    uint32_t pw[NKC][4];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {(__bf16)s[kc >> 1][8 * (kc & 1) + 2 * e], (__bf16)s[kc >> 1][8 * (kc & 1) + 2 * e + 1]};
+        pw[kc][e] = __builtin_bit_cast(uint32_t, pr);
+      }
+    float pbf[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pbf[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kc][e]), kOnesBf16x2, pbf[e & 1], false);
+    l_bf += pbf[0] + pbf[1];
+    const uint32_t vaddr = lds_addr(st) + (uint32_t)v_off;
+    TrReads<NDT> vr;
+    static_for<0, NKC>([&](auto kcc) {
+      constexpr int kc = decltype(kcc)::value;
+      vr.template issue<16 * kc * C::VROW, C::VROW>(vaddr);
+      vr.template wait<0>();
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 w = {pw[kc][0], pw[kc][1], pw[kc][2], pw[kc][3]};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) mma(oacc[t], vr.frag(t), pf);
+    });
+  };
+
+  int kb = kb0;
+  for (; kb < min(kb_full, kb_end); ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    block(kb, std::false_type{});
+  }
+  for (; kb < kb_end; ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    block(kb, std::true_type{});
+  }
+
+  if (!row_ok) return;
+  const float lb = l_bf + __shfl_xor(l_bf, 32);
+  const float l32 = l_32 + __shfl_xor(l_32, 32);
+  const bool seen = lb > 0.f;  // false: no key of this split is visible to the row
+  const float inv = seen ? 1.f / lb : 0.f;
+  const float lse_row = seen ? (m_run + __log2f(l32)) * 0.69314718055994531f : -INFINITY;
+  if (a.num_splits == 1) {
+    uint16_t* O = static_cast<uint16_t*>(a.o) + row * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint16_t out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) to_elem(oacc[t][4 * gq + e] * inv, out[e]);
+        *reinterpret_cast<uint2*>(O + 32 * t + 8 * gq + 4 * h) = *reinterpret_cast<const uint2*>(out);
+      }
+    if (h == 0) a.lse[row] = lse_row;
+  } else {
+    float* O = a.part_o + ((long long)split * a.rows + row) * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float4 out;
+        out.x = oacc[t][4 * gq + 0] * inv;
+        out.y = oacc[t][4 * gq + 1] * inv;
+        out.z = oacc[t][4 * gq + 2] * inv;
+        out.w = oacc[t][4 * gq + 3] * inv;
+        *reinterpret_cast<float4*>(O + 32 * t + 8 * gq + 4 * h) = out;
+      }
+    if (h == 0) a.part_lse[(long long)split * a.rows + row] = lse_row;
+  }
+}
+
+// Merge of the split partials of every row: M = max_s lse_s, w_s = exp(lse_s - M),
+// O = sum_s w_s O_s / sum_s w_s (bf16), lse = M + ln sum_s w_s. D/8 threads per
+// row, 8 columns each. Rows every split saw no key of get O = 0, lse = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(KvArgs a) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= a.rows) return;
+  const int S = a.num_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_lse[(long long)s * a.rows + row]);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float ls = a.part_lse[(long long)s * a.rows + row];
+      const float w = __expf(ls - M);  // exp(-inf) = 0 for splits the row saw no key of
+      L += w;
+      const float4* p = reinterpret_cast<const float4*>(a.part_o + ((long long)s * a.rows + row) * D + 8 * part);
+      const float4 x0 = p[0], x1 = p[1];
+      acc[0] = fmaf(w, x0.x, acc[0]);
+      acc[1] = fmaf(w, x0.y, acc[1]);
+      acc[2] = fmaf(w, x0.z, acc[2]);
+      acc[3] = fmaf(w, x0.w, acc[3]);
+      acc[4] = fmaf(w, x1.x, acc[4]);
+      acc[5] = fmaf(w, x1.y, acc[5]);
+      acc[6] = fmaf(w, x1.z, acc[6]);
+      acc[7] = fmaf(w, x1.w, acc[7]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t out[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) to_elem(acc[e] * inv, out[e]);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.o) + row * D + 8 * part) = *reinterpret_cast<const uint4*>(out);
+  if (part == 0) a.lse[row] = L > 0.f ? M + __logf(L) : -INFINITY;
+}
+
+template <int D, int NW, bool CAUSAL>
+hipError_t launch_fwd_kv_bf16(const KvArgs& a, hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  const int G = a.Hq / a.Hkv;
+  const long long nrb = ((long long)a.max_nq * G + BM - 1) / BM;
+  hipLaunchKernelGGL((fwd_kv_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)(nrb * a.num_splits), a.Hkv, a.B),
+                     dim3(64 * NW), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

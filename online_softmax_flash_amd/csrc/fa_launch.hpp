@@ -9,11 +9,35 @@ namespace fa {
 
 struct FwdArgs;
 
+// Arguments of the general forward (see fa_fwd_kv_bf16.hpp).
+struct KvArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;    // [num_splits][rows][D] fp32, when num_splits > 1
+  float* part_lse;  // [num_splits][rows]
+  const int* cu_q;  // variable-length offsets [B+1] (device), or null
+  const int* cu_k;
+  int B, Hq, Hkv;
+  int Nq, Nk;          // uniform: lengths; variable length: totals Tq, Tk
+  int max_nq, max_nk;  // largest sequence lengths (grid sizing)
+  int num_splits, split_keys;  // keys per split: a multiple of 64
+  long long rows;              // number of (batch, head, query) rows
+  float c;                     // scale * log2(e)
+};
+
+
 // Forward: picks the kernel instance for (d, causal) and launches it on stream.
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int N, int d, float c, int causal, hipStream_t stream);
 hipError_t fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, float c, int causal, hipStream_t stream);
+
+// General forward (rectangular, variable length, split keys; bf16): the
+// kernel for (d, rows per K/V head, causal), then the combine when split.
+hipError_t fwd_kv_bf16(const KvArgs& a, int d, int causal, hipStream_t stream);
 
 // Backward: D = rowsum(dO * O) into dsum, then the dK/dV and dQ kernels,
 // all on stream.

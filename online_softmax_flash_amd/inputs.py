@@ -27,6 +27,8 @@ __all__ = [
     "bits_to_f32",
     "AttnInputs",
     "make_inputs",
+    "make_kv_inputs",
+    "make_varlen_inputs",
 ]
 
 
@@ -109,3 +111,33 @@ def make_inputs(
         if do is not None:
             do = bf16_round(do)
     return AttnInputs(q=q, k=k, v=v, do=do, dtype=dtype, seed=seed, heavy_rows=heavy)
+
+
+def make_kv_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int) -> AttnInputs:
+    """Rectangular problem: Q ``[B, Hq, Nq, d]``, K and V ``[B, Hkv, Nk, d]``,
+    i.i.d. standard normal float32 draws in that order, rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=None, dtype="bf16", seed=seed,
+                      heavy_rows=None)
+
+
+def make_varlen_inputs(Hq: int, Hkv: int, cu_q, cu_k, d: int, seed: int) -> AttnInputs:
+    """Variable-length batch packed along the token axis: Q ``[Hq, Tq, d]``,
+    K and V ``[Hkv, Tk, d]`` with Tq = cu_q[-1], Tk = cu_k[-1]; i.i.d. standard
+    normal float32 draws in that order, rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Hq, int(cu_q[-1]), d), dtype=np.float32)
+    k = rng.standard_normal((Hkv, int(cu_k[-1]), d), dtype=np.float32)
+    v = rng.standard_normal((Hkv, int(cu_k[-1]), d), dtype=np.float32)
+    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=None, dtype="bf16", seed=seed,
+                      heavy_rows=None)
+
+
+def varlen_lengths(n_seq: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths of a variable-length batch: log-uniform integers in
+    [lo, hi] (many short sequences, a few long ones), seeded."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi + 1), size=n_seq)).astype(np.int64).clip(lo, hi)

@@ -67,3 +67,43 @@ WORKLOADS = {
 
 # The workload the headline throughput is quoted on.
 HEADLINE = "long_8k"
+
+
+@dataclass(frozen=True)
+class KvWorkload:
+    """Rectangular or variable-length problems of the general forward (bottom-right
+    causal mask), with the key range split over workgroups (num_splits = 0: the
+    library's choice). ``lengths_seed`` > 0 makes it a variable-length batch of
+    B sequences, query and key lengths drawn by inputs.varlen_lengths in
+    [Nq_lo, Nq] and [Nk_lo, Nk]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    num_splits: int = 0
+    Nq_lo: int = 0
+    Nk_lo: int = 0
+    lengths_seed: int = 0
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+KV_WORKLOADS = {
+    w.name: w
+    for w in [
+        KvWorkload("decode_32k", 8, 32, 8, 1, 32768, 128, True, 5,
+                   note="one decode step: 8 sequences, 32 query heads on 8 K/V heads, 32768 cached keys"),
+        KvWorkload("chunk_2k_8k", 1, 32, 8, 2048, 8192, 128, True, 6,
+                   note="chunked prefill: the last 2048 queries of an 8192-token causal prefix"),
+        KvWorkload("varlen_mix", 16, 32, 8, 4096, 4096, 128, True, 7, Nq_lo=64, Nk_lo=64, lengths_seed=8,
+                   note="16 sequences, log-uniform lengths in [64, 4096], queries = keys per sequence"),
+    ]
+}

@@ -9,7 +9,8 @@ Everything is plain numpy in float64:
 
 * :mod:`oracle.attention` -- the definition: the full score matrix is formed,
   masked, softmaxed and applied to V, one (batch, head) at a time; and the
-  analytic backward obtained from that definition by the chain rule.
+  analytic backward obtained from that definition by the chain rule; the
+  merge of partial results over key ranges; variable-length batches.
 * :mod:`oracle.online_fold` -- a separate implementation of the online-softmax
   recurrence (running max, running normaliser, rescaled running output), key
   block by key block. It does not import :mod:`oracle.attention`.
@@ -27,5 +28,7 @@ from .attention import (  # noqa: F401
     attn_bwd_group,
     attn_bwd_analytic,
     kv_head,
+    merge_partials,
+    attn_fwd_varlen,
 )
 from .online_fold import attn_fwd_online_fold, fold_head  # noqa: F401

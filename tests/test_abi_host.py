@@ -110,3 +110,60 @@ def test_workspace_bytes_linear_in_n():
     assert ws(0, 1, 1, 1, 64) == 0
     assert ws(1, 3, 2, 1, 64) == 0
     assert ws(1, 1, 1, 1, 100) == 0
+
+
+def _kv(ptrs=(FAKE,) * 5, shape=(2, 8, 2, 3, 100, 128), scale=0.1, causal=1, splits=1, ws=None, ws_bytes=0):
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    w = ctypes.c_void_p(ws) if ws else None
+    return lib.flash_attn_fwd_kv(*p, *shape, ctypes.c_float(scale), causal, splits, w, ctypes.c_size_t(ws_bytes),
+                                 None)
+
+
+def _varlen(cu=(FAKE, FAKE), shape=(2, 8, 2, 50, 60, 30, 40, 128), splits=1):
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(FAKE)] * 5
+    c = [ctypes.c_void_p(x) if x else None for x in cu]
+    return lib.flash_attn_fwd_varlen(*p, *c, *shape, ctypes.c_float(0.1), 1, splits, None, ctypes.c_size_t(0), None)
+
+
+def test_kv_rejects_bad_arguments():
+    assert _kv(ptrs=(FAKE, 0, FAKE, FAKE, FAKE)) == STATUS["FA_ERR_NULL"]
+    assert _kv(ptrs=(FAKE, FAKE, FAKE + 4, FAKE, FAKE)) == STATUS["FA_ERR_ALIGN"]
+    assert _kv(shape=(2, 8, 3, 3, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _kv(shape=(2, 8, 2, 0, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _kv(shape=(2, 8, 2, 3, 0, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _kv(shape=(2, 8, 2, 3, 100, 96)) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert _kv(causal=2) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert _kv(scale=math.inf) == STATUS["FA_ERR_SCALE"]
+    assert _kv(splits=-1) == STATUS["FA_ERR_SHAPE"]
+    assert _kv(splits=257) == STATUS["FA_ERR_SHAPE"]
+    # Split keys need the partials' workspace, of at least the stated size, aligned.
+    rows = 2 * 8 * 3
+    need = fa.flash_attn_fwd_kv_workspace_bytes(rows, 128, 4)
+    assert _kv(splits=4) == STATUS["FA_ERR_WORKSPACE"]
+    assert _kv(splits=4, ws=FAKE, ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
+    assert _kv(splits=4, ws=FAKE + 8, ws_bytes=need) == STATUS["FA_ERR_ALIGN"]
+
+
+def test_varlen_rejects_bad_arguments():
+    assert _varlen(cu=(0, FAKE)) == STATUS["FA_ERR_NULL"]
+    assert _varlen(cu=(FAKE, 0)) == STATUS["FA_ERR_NULL"]
+    assert _varlen(shape=(0, 8, 2, 50, 60, 30, 40, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _varlen(shape=(2, 8, 2, 50, 60, 0, 40, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _varlen(shape=(2, 8, 2, 50, 60, 30, 40, 80)) == STATUS["FA_ERR_UNSUPPORTED"]
+
+
+def test_kv_workspace_and_split_choice():
+    ws = fa.flash_attn_fwd_kv_workspace_bytes
+    assert ws(10, 128, 1) == 0
+    assert ws(10, 128, 3) == ((3 * 10 * 128 * 4 + 255) // 256) * 256 + ((3 * 10 * 4 + 255) // 256) * 256
+    assert ws(0, 128, 3) == 0 and ws(10, 100, 3) == 0 and ws(10, 128, 0) == 0 and ws(10, 128, 257) == 0
+    ns = fa.flash_attn_fwd_kv_num_splits
+    # A decode step of 8 sequences x 8 K/V heads is 64 workgroups: split the keys.
+    s = ns(8, 32, 8, 1, 32768, 128)
+    assert 2 <= s <= 256 and s <= 32768 // 256
+    # A long prefill fills the chip without splitting; short key ranges are never split.
+    assert ns(1, 32, 32, 8192, 8192, 128) == 1
+    assert ns(1, 8, 8, 1, 300, 128) == 1
+    assert ns(1, 8, 3, 1, 300, 128) == 0
