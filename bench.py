@@ -39,7 +39,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the headline one); the general-forward workloads "
+                         "(decode_32k, chunk_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
@@ -98,6 +100,10 @@ def main():
         sys.exit(1)
     fa.load_library()  # fails loudly when the HIP library is not built
 
+    from online_softmax_flash_amd.workloads import KV_WORKLOADS
+    if args.workload in KV_WORKLOADS:
+        print(json.dumps(bench_kv(args, KV_WORKLOADS[args.workload])))
+        return
     w = WORKLOADS[args.workload or HEADLINE]
     causal = w.causal[-1]
     inp = make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, seed=w.seed, dtype=w.dtype, heavy_frac=w.heavy_frac,
@@ -194,6 +200,111 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, inp, causal, args.cpu_seconds)
 
     print(json.dumps(result))
+
+
+def bench_kv(args, w):
+    """One step = one general forward (all splits and the combine) over the workload."""
+    import torch
+    import online_softmax_flash_amd as fa
+    from online_softmax_flash_amd.inputs import make_kv_inputs, make_varlen_inputs
+
+    dev = torch.device("cuda:0")
+    lens = w.lengths()
+    if w.lengths_seed:
+        cu = np.concatenate([[0], np.cumsum([nq for nq, _ in lens])]).astype(np.int64)
+        inp = make_varlen_inputs(w.Hq, w.Hkv, cu, cu, w.d, w.seed)
+        cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+        max_q = int(max(nq for nq, _ in lens))
+        max_k = int(max(nk for _, nk in lens))
+        rows = w.Hq * int(cu[-1])
+    else:
+        inp = make_kv_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+        max_q, max_k = w.Nq, w.Nk
+        rows = w.B * w.Hq * w.Nq
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (inp.q, inp.k, inp.v))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    B = len(lens)
+    splits = w.num_splits or fa.flash_attn_fwd_kv_num_splits(B, w.Hq, w.Hkv, max_q, max_k, w.d)
+    nws = fa.flash_attn_fwd_kv_workspace_bytes(rows, w.d, splits)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
+    def step():
+        if w.lengths_seed:
+            fa.flash_attn_fwd_varlen(q, k, v, o, lse, cu_t, cu_t, max_q, max_k, w.scale, w.causal, splits, ws)
+        else:
+            fa.flash_attn_fwd_kv(q, k, v, o, lse, w.scale, w.causal, splits, ws)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.fwd_flops()
+    nbytes = w.min_bytes()
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    hbm = w.Nq * (w.Hq // w.Hkv) <= 32 and not w.lengths_seed  # decode: reading K and V is the work
+    result = {
+        "metric": ("attention decode HBM GB/s (bf16, split keys)" if hbm
+                   else "attention fwd TFLOP/s (bf16, general forward)"),
+        "value": round(gbs if hbm else tflops, 3),
+        "unit": "GB/s" if hbm else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": max_q, "Nk": max_k, "d": w.d,
+                   "causal": w.causal, "varlen": bool(w.lengths_seed), "num_splits": splits, "seed": w.seed,
+                   "credited_flops": flops, "min_hbm_bytes": nbytes, "tflops": round(tflops, 3),
+                   "gbs": round(gbs, 3)},
+        "roofline": ({"bound": "hbm", "kernel": "fwd_kv_bf16_kernel + fwd_combine_kernel", "achieved": round(gbs, 3),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                     if hbm else
+                     {"bound": "mfma", "kernel": "fwd_kv_bf16_kernel", "achieved": round(tflops, 3),
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                      "traffic": None}),
+        "wall_s_timed_region": round(wall_s, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        G = w.Hq // w.Hkv
+        t0 = time.perf_counter()
+        done = 0
+        pairs = [(b, hq) for b in range(B) for hq in range(w.Hq)]
+        for b, hq in pairs:
+            if w.lengths_seed:
+                t_a, t_b = int(cu[b]), int(cu[b + 1])
+                oracle.attn_fwd_head(inp.q[hq, t_a:t_b], inp.k[hq // G, t_a:t_b], inp.v[hq // G, t_a:t_b], w.scale,
+                                     w.causal)
+            else:
+                oracle.attn_fwd_head(inp.q[b, hq], inp.k[b, hq // G], inp.v[b, hq // G], w.scale, w.causal)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        frac = done / len(pairs)  # heads are of equal work except in the variable-length batch
+        if w.lengths_seed:
+            per = [w.Hq and (nq * nk) for nq, nk in lens]
+            frac = sum(per[b] for b, _ in pairs[:done]) / (w.Hq * sum(per))
+        val = (nbytes * frac / dt / 1e9) if hbm else (flops * frac / dt / 1e12)
+        result["cpu_baseline"] = {"value": round(val, 6), "unit": result["unit"], "cores": os.cpu_count(),
+                                  "kind": "oracle",
+                                  "sample": f"{done} of {len(pairs)} (sequence, head) slices, fp64 numpy, {dt:.1f} s"}
+    return result
 
 
 def _stored_traffic(path):

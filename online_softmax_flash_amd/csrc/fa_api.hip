@@ -77,13 +77,14 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
 
 // Split count for the general forward: one unless the (batch, K/V head, row
 // block) workgroups are too few to fill the chip; then enough splits for about
-// four workgroups per compute unit, each split at least 256 keys.
+// four workgroups per compute unit (eight for one-wave decoding workgroups,
+// whose work is streaming K and V), each split at least 256 keys.
 int kv_splits_auto(int B, int Hq, int Hkv, int max_nq, int max_nk) {
   const long long G = Hq / Hkv;
   const long long rows = (long long)max_nq * G;
   const long long bm = rows <= 32 ? 32 : 128;
   const long long wgs = (long long)B * Hkv * ((rows + bm - 1) / bm);
-  const long long target = 4 * 256;
+  const long long target = (rows <= 32 ? 8 : 4) * 256;
   if (wgs >= target / 2 || max_nk <= 512) return 1;
   long long s = (target + wgs - 1) / wgs;
   s = s < (max_nk + 255) / 256 ? s : (max_nk + 255) / 256;

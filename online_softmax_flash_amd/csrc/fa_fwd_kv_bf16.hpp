@@ -18,8 +18,9 @@
 // r / G of query head hkv*G + r % G. A decode step (Nq = 1) thus fills G rows
 // of a tile instead of one, and every K/V block staged in LDS serves all of
 // them. Data movement is that of the square bf16 forward (fa_fwd_bf16.hpp):
-// K and V blocks of 64 keys direct to LDS, double-buffered, padded rows, V
-// read with transposing reads; Q rows in registers as B operands.
+// K and V blocks of 64 keys (32 for one-wave decoding workgroups) direct to
+// LDS, double-buffered, padded rows, V read with transposing reads; Q rows in
+// registers as B operands.
 //
 // Conventions: query i of a sequence with nq queries and nk keys sees key j
 // iff j <= i + nk - nq (causal) and j < nk; a row that sees no key gets O = 0
@@ -60,9 +61,8 @@ struct LeanDma {
   }
 };
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
-  constexpr int BN = 64;
   using C = Bf16FwdCfg<D, BN, NW>;
   constexpr int BM = C::BM;
   constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
@@ -288,26 +288,31 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
 
 // Merge of the split partials of every row: M = max_s lse_s, w_s = exp(lse_s - M),
 // O = sum_s w_s O_s / sum_s w_s (bf16), lse = M + ln sum_s w_s. D/8 threads per
-// row, 8 columns each. Rows every split saw no key of get O = 0, lse = -inf.
+// row, 8 columns each, 64 threads per workgroup (decoding has few rows: many
+// small workgroups); the split loops are unrolled so that several partials
+// are in flight per thread. Rows every split saw no key of get O = 0, lse = -inf.
 template <int D>
-__global__ __launch_bounds__(256) void fwd_combine_kernel(KvArgs a) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+__global__ __launch_bounds__(64) void fwd_combine_kernel(KvArgs a) {
+  constexpr int TPR = D / 8, RPB = 64 / TPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   if (row >= a.rows) return;
   const int S = a.num_splits;
+  const float* pl = a.part_lse + row;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_lse[(long long)s * a.rows + row]);
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pl[(long long)s * a.rows]);
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
+    const float* po = a.part_o + row * D + 8 * part;
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
-      const float ls = a.part_lse[(long long)s * a.rows + row];
-      const float w = __expf(ls - M);  // exp(-inf) = 0 for splits the row saw no key of
+      const float w = __expf(pl[(long long)s * a.rows] - M);  // 0 for splits the row saw no key of
       L += w;
-      const float4* p = reinterpret_cast<const float4*>(a.part_o + ((long long)s * a.rows + row) * D + 8 * part);
+      const float4* p = reinterpret_cast<const float4*>(po + (long long)s * a.rows * D);
       const float4 x0 = p[0], x1 = p[1];
       acc[0] = fmaf(w, x0.x, acc[0]);
       acc[1] = fmaf(w, x0.y, acc[1]);
@@ -330,14 +335,17 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(KvArgs a) {
 template <int D, int NW, bool CAUSAL>
 hipError_t launch_fwd_kv_bf16(const KvArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * NW;
+  // Key blocks of 64, or of 32 for one-wave workgroups (decoding): half the
+  // LDS per workgroup, so twice as many workgroups stream K and V per CU.
+  constexpr int BN = NW == 1 ? 32 : 64;
   const int G = a.Hq / a.Hkv;
   const long long nrb = ((long long)a.max_nq * G + BM - 1) / BM;
-  hipLaunchKernelGGL((fwd_kv_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)(nrb * a.num_splits), a.Hkv, a.B),
+  hipLaunchKernelGGL((fwd_kv_bf16_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)(nrb * a.num_splits), a.Hkv, a.B),
                      dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  constexpr int RPB = 64 / (D / 8);
+  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -95,6 +95,36 @@ class KvWorkload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
+    def lengths(self):
+        """Per-sequence (query, key) lengths."""
+        if not self.lengths_seed:
+            return [(self.Nq, self.Nk)] * self.B
+        from .inputs import varlen_lengths
+        lens = varlen_lengths(self.B, self.Nq_lo, self.Nq, self.lengths_seed)
+        return [(int(n), int(n)) for n in lens]
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the mask keeps, summed over sequences (one head)."""
+        tot = 0
+        for nq, nk in self.lengths():
+            if not self.causal:
+                tot += nq * nk
+            else:
+                # query i sees min(nk, max(0, i + nk - nq + 1)) keys
+                for i in range(nq):
+                    tot += min(nk, max(0, i + nk - nq + 1))
+        return tot
+
+    def fwd_flops(self) -> float:
+        """Credited flops: 4*d per visible (query, key) pair and query head."""
+        return 4.0 * self.d * self.Hq * self.visible_pairs()
+
+    def min_bytes(self) -> int:
+        """Smallest HBM traffic: read Q, K, V once, write O (bf16) and lse once."""
+        tq = sum(nq for nq, _ in self.lengths())
+        tk = sum(nk for _, nk in self.lengths())
+        return 2 * (2 * self.Hq * tq * self.d) + 2 * (2 * self.Hkv * tk * self.d) + 4 * self.Hq * tq
+
 
 KV_WORKLOADS = {
     w.name: w
