@@ -44,6 +44,8 @@ def parse():
                          "(decode_32k, chunk_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="skip the three-pass materialising baseline timed on the same inputs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration runs)")
@@ -195,6 +197,31 @@ def main():
                                   "pct_of_peak": round(100.0 * btf / PEAK_BF16_TFLOPS, 2)}
         except fa.FlashAttnError as e:
             result["backward"] = {"error": str(e)}
+
+    if not args.no_naive and w.dtype == "bf16":
+        # The materialising baseline on the same inputs: scores and weights of
+        # every pair go through HBM. Quadratic workspace, allocated here.
+        nws = fa.flash_attn_naive_workspace_bytes(w.B, w.Hq, w.N)
+        free, _ = torch.cuda.mem_get_info()
+        if nws + (1 << 30) < free:
+            ws_n = torch.empty(nws, dtype=torch.uint8, device=dev)
+            o_n, lse_n = torch.empty_like(q), torch.empty_like(lse)
+            fa.flash_attn_naive_fwd(q, k, v, o_n, lse_n, w.scale, causal, ws_n)
+            torch.cuda.synchronize()
+            nn = max(3, args.steps // 5)
+            ev0.record(stream)
+            for _ in range(nn):
+                fa.flash_attn_naive_fwd(q, k, v, o_n, lse_n, w.scale, causal, ws_n)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            nms = ev0.elapsed_time(ev1) / nn
+            result["naive_baseline"] = {"ms": round(nms, 5), "tflops": round(flops / (nms * 1e-3) / 1e12, 3),
+                                        "fused_speedup": round(nms / ms, 3), "steps": nn,
+                                        "workspace_bytes": nws,
+                                        "kernels": "naive_scores_kernel, naive_softmax_kernel, naive_pv_kernel"}
+            del ws_n, o_n, lse_n
+        else:
+            result["naive_baseline"] = {"skipped": f"needs {nws} bytes of workspace"}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, causal, args.cpu_seconds)

@@ -152,6 +152,26 @@ int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 size_t flash_attn_fwd_kv_workspace_bytes(long long rows, int d, int num_splits);
 
 /*
+ * Standard (materialising) attention in three passes, bf16 storage: the
+ * baseline the method removes (fanfani.net "FlashAttention", section "The
+ * bottleneck was never the arithmetic": scores written to slow memory, read
+ * back for the mask and the softmax, the weights written and read back for
+ * the product with V). Same inputs, outputs and conventions as
+ * flash_attn_fwd (square, top-left causal mask), same O and lse up to
+ * rounding; it exists to measure on the same chip the traffic and time the
+ * fused forward saves.
+ *   workspace: caller-owned device buffer of flash_attn_naive_workspace_bytes
+ *     (B*Hq*N*N fp32 scores then B*Hq*N*N bf16 weights, each rounded up to 256
+ *     bytes): quadratic in N by design.
+ * Errors as flash_attn_fwd; FA_ERR_SHAPE also when B*Hq*N exceeds 2^31-1,
+ * FA_ERR_WORKSPACE for a missing or short workspace.
+ */
+int flash_attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t flash_attn_naive_workspace_bytes(int B, int Hq, int N);
+
+/*
  * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these
  * sizes: two fp32 per query row (D_i = sum_c dO_ic O_ic, and lse_i * log2(e)),
  * 4*(R64 + R) bytes with R = B*Hq*N and R64 = R rounded up to a multiple of

@@ -29,6 +29,8 @@ __all__ = [
     "flash_attn_fwd_kv_workspace_bytes",
     "attention_forward",
     "attention_forward_kv",
+    "flash_attn_naive_fwd",
+    "flash_attn_naive_workspace_bytes",
     "attention_forward_varlen",
     "attention_backward",
 ]
@@ -78,6 +80,10 @@ def load_library():
     lib.flash_attn_fwd_kv_num_splits.restype = I
     lib.flash_attn_fwd_kv_workspace_bytes.argtypes = [L, I, I]
     lib.flash_attn_fwd_kv_workspace_bytes.restype = Z
+    lib.flash_attn_naive_fwd.argtypes = [P] * 5 + [I] * 5 + [F, I, P, Z, P]
+    lib.flash_attn_naive_fwd.restype = I
+    lib.flash_attn_naive_workspace_bytes.argtypes = [I, I, I]
+    lib.flash_attn_naive_workspace_bytes.restype = Z
     lib.flash_attn_status_str.argtypes = [I]
     lib.flash_attn_status_str.restype = ctypes.c_char_p
     _LIB = lib
@@ -290,3 +296,22 @@ def attention_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
     flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal,
                           splits, ws, stream)
     return o, lse
+
+
+def flash_attn_naive_workspace_bytes(B, Hq, N) -> int:
+    return int(load_library().flash_attn_naive_workspace_bytes(int(B), int(Hq), int(N)))
+
+
+def flash_attn_naive_fwd(q, k, v, o, lse, scale, causal, workspace, stream=None):
+    """Three-pass materialising baseline (bf16): same arguments as flash_attn_fwd
+    plus a workspace of flash_attn_naive_workspace_bytes(B, Hq, N) bytes."""
+    import torch
+    _check(q, k, v, o, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    _check(workspace)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    st = load_library().flash_attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                             float(scale), int(bool(causal)), _ptr(workspace), _ws_size(workspace),
+                                             _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_naive_fwd", st)

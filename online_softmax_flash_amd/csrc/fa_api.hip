@@ -217,6 +217,32 @@ int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
                    scale, causal, num_splits, workspace, workspace_bytes, stream);
 }
 
+size_t flash_attn_naive_workspace_bytes(int B, int Hq, int N) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  const size_t pairs = (size_t)B * Hq * N * N;
+  return ((pairs * 4 + 255) & ~(size_t)255) + ((pairs * 2 + 255) & ~(size_t)255);
+}
+
+int flash_attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse};
+  int st = check_ptrs(ptrs, 5);
+  if (st == FA_OK) st = check_shape(B, Hq, Hkv, N, d, causal);
+  if (st == FA_OK && (long long)B * Hq * N > 0x7fffffffLL) st = FA_ERR_SHAPE;
+  if (st == FA_OK) st = check_scale(scale);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if (workspace_bytes < flash_attn_naive_workspace_bytes(B, Hq, N)) return FA_ERR_WORKSPACE;
+  const size_t pairs = (size_t)B * Hq * N * N;
+  float* s = static_cast<float*>(workspace);
+  uint16_t* p = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + ((pairs * 4 + 255) & ~(size_t)255));
+  const hipError_t e = fa::naive_bf16(q, k, v, o, lse, s, p, B, Hq, Hkv, N, d, scale, causal,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* flash_attn_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

@@ -39,6 +39,11 @@ hipError_t fwd_f32(const void* q, const void* k, const void* v, void* o, float* 
 // kernel for (d, rows per K/V head, causal), then the combine when split.
 hipError_t fwd_kv_bf16(const KvArgs& a, int d, int causal, hipStream_t stream);
 
+// Three-pass materialising baseline (bf16): S (fp32) and P (bf16) of every
+// (query, key) pair go through the caller's workspace s and p.
+hipError_t naive_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* s, uint16_t* p,
+                      int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
+
 // Backward: D = rowsum(dO * O) into dsum, then the dK/dV and dQ kernels,
 // all on stream.
 hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,

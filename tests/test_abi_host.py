@@ -167,3 +167,22 @@ def test_kv_workspace_and_split_choice():
     assert ns(1, 32, 32, 8192, 8192, 128) == 1
     assert ns(1, 8, 8, 1, 300, 128) == 1
     assert ns(1, 8, 3, 1, 300, 128) == 0
+
+
+def test_naive_rejects_bad_arguments_and_sizes_workspace():
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(FAKE)] * 5
+
+    def call(shape=(1, 4, 2, 100, 128), causal=1, ws=FAKE, nbytes=None):
+        n = fa.flash_attn_naive_workspace_bytes(shape[0], shape[1], shape[3]) if nbytes is None else nbytes
+        w = ctypes.c_void_p(ws) if ws else None
+        return lib.flash_attn_naive_fwd(*p, *shape, ctypes.c_float(0.1), causal, w, ctypes.c_size_t(n), None)
+
+    assert call(shape=(1, 4, 3, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert call(shape=(1, 4, 2, 100, 32)) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert call(ws=0) == STATUS["FA_ERR_WORKSPACE"]
+    assert call(nbytes=1000) == STATUS["FA_ERR_WORKSPACE"]
+    assert call(ws=FAKE + 4) == STATUS["FA_ERR_ALIGN"]
+    # quadratic in N: N*N fp32 scores plus N*N bf16 weights per head
+    assert fa.flash_attn_naive_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 4096 * 6
+    assert fa.flash_attn_naive_workspace_bytes(0, 16, 4096) == 0
