@@ -102,6 +102,15 @@ def main():
         sys.exit(1)
     fa.load_library()  # fails loudly when the HIP library is not built
 
+    if args.copy_calibration_mib:
+        # A device copy of known size first: counter runs scale by what it reads and writes.
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     from online_softmax_flash_amd.workloads import KV_WORKLOADS
     if args.workload in KV_WORKLOADS:
         print(json.dumps(bench_kv(args, KV_WORKLOADS[args.workload])))
@@ -116,14 +125,6 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
     fwd = fa.flash_attn_fwd if w.dtype == "bf16" else fa.flash_attn_fwd_f32
-
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -349,14 +350,21 @@ def _stored_traffic(path):
     return int(t.group(1))
 
 
+# Sources and build flags of the headline forward kernel: stored counter data
+# is used only while these are unchanged.
+FWD_SOURCES = ("fa_device.hpp", "fa_fwd.hpp", "fa_fwd_bf16.hpp", "fa_fwd_bf16.hip")
+
+
 def _kernel_sha() -> str:
-    """Hash of the kernel sources, to tell whether stored counter data is current."""
+    """Hash of the headline forward's sources and flags, to tell whether stored counter data is current."""
     import hashlib
+    from online_softmax_flash_amd import build as b
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "online_softmax_flash_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FWD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    h.update(repr(b.COMMON + b.DEVICE_FLAGS + b.EXTRA_FLAGS.get("fa_fwd_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
