@@ -9,9 +9,11 @@
 // partial result (o / l in fp32, lse = m + ln l) and fwd_combine_kernel merges
 // them with the recurrence's own rescale step: each partial enters like one
 // block whose maximum is its lse and whose exponential sum is 1. That is the
-// step that serves decoding (few queries, a long key/value cache: the work is
-// reading K and V, section "What changed in practice" on the pages' serving
-// remarks), where one (batch, K/V head) alone cannot fill the chip.
+// step that serves decoding (few queries, a long key/value cache: the cache,
+// not the score matrix, is what limits serving -- fanfani.net, the closing
+// paragraph of section "The backward pass, and where the memory saving comes
+// from", and section "What to carry forward"), where one (batch, K/V head)
+// alone cannot fill the chip.
 //
 // Rows. The G query heads that share a K/V head are packed into the rows of
 // one workgroup: packed row r of (batch b, K/V head hkv) is query position
