@@ -95,6 +95,29 @@ struct Bf16FwdCfg {
   static constexpr int VBYTES = BN * VROW;
 };
 
+// Wave-uniform 64-bit value in scalar registers (readfirstlane returns int:
+// convert through uint32_t so that the low half is zero-extended).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+}
+
+// One direct global->LDS copy of 16 bytes per lane: lane i reads global
+// gbase + voff (bytes) and writes LDS lds_base + 16*i. lds_base and gbase are
+// wave-uniform (scalar registers; lds_base goes through M0). The compiler
+// does not see this write to LDS: callers wait for it (vmcnt) and synchronise
+// before the destination is read.
+__device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, uint64_t gbase) {
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0v), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // Direct global->LDS copy of rows [0, BN) of a row-major bf16 [*, D] matrix
 // into an LDS block with ROWB-byte rows (2*D data bytes + padding). The block
 // is a sequence of 16-byte slots; wave-instruction n fills slots
@@ -121,8 +144,13 @@ struct BlockDma {
     }
   }
   // Rows >= valid read row valid - 1 (finite data; the kernel masks those keys).
+  // Issued in scalar-base form (block base address and LDS destination in
+  // scalar registers, a 32-bit per-lane byte offset), so no per-lane 64-bit
+  // address arithmetic is spent per instruction.
   template <bool FULL>
   __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave) const {
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
+    const uint64_t gs = uniform_u64((uint64_t)g);
 #pragma unroll
     for (int j = 0; j < NPER; ++j) {
       const int n = wave + j * NW;
@@ -130,7 +158,37 @@ struct BlockDma {
         if (off[j] >= 0) {
           int e = off[j];
           if (!FULL && row[j] >= valid) e -= (row[j] - valid + 1) * D;
-          __builtin_amdgcn_global_load_lds(g + e, (lds_void_t*)(lds + n * 1024), 16, 0, 0);
+          dma16(lb + (uint32_t)n * 1024u, (uint32_t)e * 2u, gs);
+        }
+      }
+    }
+  }
+};
+
+// Direct global->LDS copy of rows [0, BN) of a row-major bf16 [*, D] matrix
+// into BN rows of ROWB bytes, in the slot order of BlockDma (wave-instruction
+// n fills 16-byte slots 64n .. 64n+63; padding slots are skipped), but with
+// each lane's source offset recomputed at every call instead of held in
+// registers: a workgroup of one wave issues all the block's instructions, and
+// keeping their offsets would cost two registers per instruction.
+template <int D, int BN, int ROWB, int NW>
+struct LeanDma {
+  static constexpr int SPR = ROWB / 16;
+  static constexpr int CPR = 2 * D / 16;
+  static constexpr int NINSTR = (BN * SPR + 63) / 64;
+  template <bool FULL>
+  __device__ __forceinline__ static void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) {
+    asm volatile("" : "+v"(lane));  // recompute below on every call
+    const uint64_t gs = uniform_u64((uint64_t)g);
+#pragma unroll
+    for (int n0 = 0; n0 < NINSTR; n0 += NW) {
+      const int n = n0 + wave;
+      if (n0 + NW <= NINSTR || n < NINSTR) {  // wave-uniform
+        const int slot = n * 64 + lane;
+        const int r = slot / SPR, c = slot - r * SPR;
+        if (c < CPR && r < BN) {
+          const int rr = (!FULL && r >= valid) ? valid - 1 : r;
+          dma16(lds_addr(lds) + (uint32_t)n * 1024u, (uint32_t)(rr * D + c * 8) * 2u, gs);
         }
       }
     }

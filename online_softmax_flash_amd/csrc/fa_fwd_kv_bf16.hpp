@@ -34,35 +34,6 @@
 
 namespace fa {
 
-// Direct global->LDS copy of rows [0, BN) of a row-major bf16 [*, D] matrix
-// into BN rows of ROWB bytes, in the slot order of BlockDma (wave-instruction
-// n fills 16-byte slots 64n .. 64n+63; padding slots are skipped), but with
-// each lane's source offset recomputed at every call instead of held in
-// registers: a workgroup of one wave issues all the block's instructions, and
-// keeping their offsets would cost two registers per instruction.
-template <int D, int BN, int ROWB, int NW>
-struct LeanDma {
-  static constexpr int SPR = ROWB / 16;
-  static constexpr int CPR = 2 * D / 16;
-  static constexpr int NINSTR = (BN * SPR + 63) / 64;
-  template <bool FULL>
-  __device__ __forceinline__ static void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) {
-    asm volatile("" : "+v"(lane));  // recompute below on every call
-#pragma unroll
-    for (int n0 = 0; n0 < NINSTR; n0 += NW) {
-      const int n = n0 + wave;
-      if (n0 + NW <= NINSTR || n < NINSTR) {  // wave-uniform
-        const int slot = n * 64 + lane;
-        const int r = slot / SPR, c = slot - r * SPR;
-        if (c < CPR && r < BN) {
-          const int rr = (!FULL && r >= valid) ? valid - 1 : r;
-          __builtin_amdgcn_global_load_lds(g + rr * D + c * 8, (lds_void_t*)(lds + n * 1024), 16, 0, 0);
-        }
-      }
-    }
-  }
-};
-
 template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   using C = Bf16FwdCfg<D, BN, NW>;
