@@ -134,12 +134,28 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
     if (CAUSAL && k0 > wave_kmax) return;
     const uint8_t* st = smem + (kb & 1) * STAGE;
     f32x16 s[NKT];
+    {
+      bf16x8 kf[NKT][NF];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      s[kt] = zero16();
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-        mma(s[kt], *reinterpret_cast<const bf16x8*>(st + k_off + 32 * kt * C::KROW + 32 * f), qf[f]);
+        for (int f = 0; f < NF; ++f) kf[kt][f] = *reinterpret_cast<const bf16x8*>(st + k_off + 32 * kt * C::KROW + 32 * f);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        s[kt] = zero16();
+#pragma unroll
+        for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
+      }
+      // The first tile's K reads, then each later read beside one product.
+      if constexpr (D <= 128) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+#pragma unroll
+        for (int i = 0; i < (NKT - 1) * NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+      }
     }
     bool keep[NKT][16];
     if constexpr (MASKED) {
@@ -196,17 +212,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
       for (int e = 0; e < 4; ++e)
         pbf[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kc][e]), kOnesBf16x2, pbf[e & 1], false);
     l_bf += pbf[0] + pbf[1];
+    // V fragments of chunk kc+1 are requested before the products of chunk kc
+    // (registers permitting).
     const uint32_t vaddr = lds_addr(st) + (uint32_t)v_off;
-    TrReads<NDT> vr;
+    constexpr bool VPIPE = D <= 128;
+    TrReads<NDT> vr[VPIPE ? 2 : 1];
+    vr[0].template issue<0, C::VROW>(vaddr);
     static_for<0, NKC>([&](auto kcc) {
       constexpr int kc = decltype(kcc)::value;
-      vr.template issue<16 * kc * C::VROW, C::VROW>(vaddr);
-      vr.template wait<0>();
+      constexpr int cur = VPIPE ? (kc & 1) : 0;
+      if constexpr (VPIPE && kc + 1 < NKC) {
+        vr[(kc + 1) & 1].template issue<16 * (kc + 1) * C::VROW, C::VROW>(vaddr);
+        vr[cur].template wait<2 * NDT>();
+      } else {
+        if constexpr (!VPIPE && kc > 0) vr[0].template issue<16 * kc * C::VROW, C::VROW>(vaddr);
+        vr[cur].template wait<0>();
+      }
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 w = {pw[kc][0], pw[kc][1], pw[kc][2], pw[kc][3]};
       const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) mma(oacc[t], vr.frag(t), pf);
+      for (int t = 0; t < NDT; ++t) mma(oacc[t], vr[cur].frag(t), pf);
     });
   };
 
