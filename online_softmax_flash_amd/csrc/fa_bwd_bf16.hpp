@@ -179,23 +179,35 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
     // (causal) every key of the pair follows every query of it.
     const bool need0 = !CAUSAL || q0 + 31 >= kw0;
     const bool need1 = q0 + 32 < N && (!CAUSAL || q0 + 63 >= kw0);
+    // Both roles run the same products on role-selected tiles, so that the
+    // accumulators stay in one set of registers:
+    //   x = rows . kvf:     S = Q K^T (P wave) or dP = dO V^T (dS wave);
+    //   acc += tr . bfr:    dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
+    const uint8_t* qs = st;
+    const uint8_t* os = st + TILE;
+    const uint8_t* rows = pwave ? qs : os;
+    const uint8_t* trs = pwave ? os : qs;
+    f32x16 x[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      x[sub] = zero16();
+      if (!(sub ? need1 : need0)) continue;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) mma(x[sub], *reinterpret_cast<const bf16x8*>(rows + sub * 32 * RS + row_off + 32 * f), kvf[f]);
+    }
+    bf16x8 bfr[2][2];
     if (pwave) {
-      // S = Q K^T -> P, for both subtiles; P to LDS and, rounded, to fragments.
-      bf16x8 pf[2][2];
+      // P = exp2(S*c - l2) with masks; P to LDS for the dS wave; bf16 fragments.
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (!(sub ? need1 : need0)) continue;
         const int qs0 = q0 + 32 * sub;
-        const uint8_t* qs = st + sub * 32 * RS;
-        f32x16 s = zero16();
-#pragma unroll
-        for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(qs + row_off + 32 * f), kvf[f]);
         float p[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * sub + 8 * r4 + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p[4 * r4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * r4 + e], c, -l4[e]));
+          for (int e = 0; e < 4; ++e) p[4 * r4 + e] = __builtin_amdgcn_exp2f(fmaf(x[sub][4 * r4 + e], c, -l4[e]));
         }
         // Masks: query row >= N, or (causal) key > query.
         if ((CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N) {
@@ -211,33 +223,13 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
           const f32x4 v = {p[4 * r4], p[4 * r4 + 1], p[4 * r4 + 2], p[4 * r4 + 3]};
           *reinterpret_cast<f32x4*>(px + sub * 4096 + r4 * 1024) = v;
         }
-        pack_frag(pf[sub][0], p);
-        pack_frag(pf[sub][1], p + 8);
+        pack_frag(bfr[sub][0], p);
+        pack_frag(bfr[sub][1], p + 8);
       }
-      __syncthreads();  // barrier 2: P visible to the dS waves
-      // dV^T += dO^T P (contraction over the 32 queries of each subtile).
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (!(sub ? need1 : need0)) continue;
-        const uint8_t* os = st + TILE + sub * 32 * RS;
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) mma(acc[t], tr_frag(os + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), pf[sub][c2]);
-      }
-    } else {
-      // dP = dO V^T for both subtiles.
-      f32x16 dp[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        dp[sub] = zero16();
-        if (!(sub ? need1 : need0)) continue;
-        const uint8_t* os = st + TILE + sub * 32 * RS;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) mma(dp[sub], *reinterpret_cast<const bf16x8*>(os + row_off + 32 * f), kvf[f]);
-      }
-      __syncthreads();  // barrier 2
-      // dS = P (dP - D), then dK^T += Q^T dS.
+    }
+    __syncthreads();  // barrier 2: P visible to the dS waves
+    if (!pwave) {
+      // dS = P (dP - D) in bf16 fragments.
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (!(sub ? need1 : need0)) continue;
@@ -247,17 +239,21 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
           const f32x4 p4 = *reinterpret_cast<const f32x4*>(px + sub * 4096 + r4 * 1024);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * sub + 8 * r4 + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = p4[e] * (dp[sub][4 * r4 + e] - d4[e]);
+          for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = p4[e] * (x[sub][4 * r4 + e] - d4[e]);
         }
-        bf16x8 dsf[2];
-        pack_frag(dsf[0], ds);
-        pack_frag(dsf[1], ds + 8);
-        const uint8_t* qs = st + sub * 32 * RS;
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) mma(acc[t], tr_frag(qs + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), dsf[c2]);
+        pack_frag(bfr[sub][0], ds);
+        pack_frag(bfr[sub][1], ds + 8);
       }
+    }
+    // acc += tr . bfr (contraction over the 32 queries of each subtile).
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      if (!(sub ? need1 : need0)) continue;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+          mma(acc[t], tr_frag(trs + sub * 32 * RS + tr_off + 16 * c2 * RS + 64 * t, 2 * RS), bfr[sub][c2]);
     }
   }
 
