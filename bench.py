@@ -364,7 +364,8 @@ def _kernel_sha() -> str:
     for f in FWD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
-    h.update(repr(b.COMMON + b.DEVICE_FLAGS + b.EXTRA_FLAGS.get("fa_fwd_bf16.hip", [])).encode())
+    flags = b.COMMON + b.DEVICE_FLAGS + b.EXTRA_FLAGS.get("fa_fwd_bf16.hip", [])
+    h.update(repr([f.replace(b.ROOT, "<root>") for f in flags]).encode())  # independent of where the tree lives
     return h.hexdigest()[:16]
 
 
