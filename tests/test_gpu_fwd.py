@@ -135,3 +135,22 @@ def test_fwd_repeatable_and_allocation_free():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
     assert free1 == free0, f"device free memory changed by {free0 - free1} bytes during a call"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fwd_very_long_single_head(d):
+    """One head at N = 65536 (the longest sequence in any test; 2^32 scores per
+    head, never stored), causal and full, on sampled rows including the first
+    and last, plus a query block boundary in the ragged layout N - 1."""
+    N = 65536 - 1  # ragged: not a multiple of any tile size
+    announce(f"fwd very long N={N} d={d} seed=61")
+    inp = make_inputs(1, 1, 1, N, d, seed=61)
+    scale = 1.0 / math.sqrt(d)
+    for causal in (True, False):
+        o, lse = run_fwd(inp, scale, causal)
+        o_h = o.float().cpu().numpy()
+        lse_h = lse.cpu().numpy()
+        rows = np.array([0, 1, 255, 256, 32767, 40000, N - 2, N - 1])
+        O_ref, L_ref = oracle.attn_fwd_head(inp.q[0, 0], inp.k[0, 0], inp.v[0, 0], scale, causal, rows=rows)
+        assert_close(o_h[0, 0, rows], O_ref, "bf16", f"N={N} d={d} causal={causal} O")
+        assert_close(lse_h[0, 0, rows], L_ref, "bf16", f"N={N} d={d} causal={causal} lse", lse=True)

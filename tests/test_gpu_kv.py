@@ -163,3 +163,18 @@ def test_varlen_full_size_sampled():
         O_ref, L_ref = oracle.attn_fwd_head(inp.q[hq, t0:t1], inp.k[hq // G, t0:t1], inp.v[hq // G, t0:t1], w.scale,
                                             w.causal, rows=rows)
         check_rows(O[hq, t0 + rows], L[hq, t0 + rows], O_ref, L_ref, f"varlen_mix seq={b} hq={hq}")
+
+
+def test_kv_decode_very_long_cache():
+    """One decode step over a 262144-key cache (MQA: 8 query heads on one K/V
+    head, d = 128) with the library's split count, against the oracle on every
+    row, and the same step with one split."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 8, 1, 1, 262144, 128
+    announce(f"kv very long cache shape={(B, Hq, Hkv, Nq, Nk, d)} seed=35")
+    inp = make_kv_inputs(B, Hq, Hkv, Nq, Nk, d, seed=35)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, inp.k, inp.v, 1.0 / math.sqrt(d), True)
+    for splits in (0, 1):
+        o, lse = fa.attention_forward_kv(q, k, v, 1.0 / math.sqrt(d), True, num_splits=splits)
+        torch.cuda.synchronize()
+        check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, f"very long cache splits={splits}")
