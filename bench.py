@@ -10,9 +10,11 @@ fp32 accumulation, 1% of query rows scaled x8, seed 2.
 
 Prints ONE JSON line: throughput in TFLOP/s (credited flops 4*B*Hq*N^2*d,
 halved when causal), the roofline of the forward kernel (MFMA-bound, against
-the 2.5 PFLOP/s dense bf16 peak), the backward pass measured the same way on
-the same inputs, and the CPU oracle timed on a bounded sample of the same
-workload (a baseline only).
+the 2.5 PFLOP/s dense bf16 peak), the per-launch median and minimum over 20
+trials of 10 launches, the GPU clock and power read by amd-smi under load,
+the backward pass measured the same way, the three-pass materialising
+baseline on the same inputs, and the CPU oracle timed on a bounded sample of
+the same workload (a baseline only).
 """
 
 from __future__ import annotations
@@ -37,8 +39,10 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # Enough untimed launches for the GPU clock to leave its idle state (with
+    # 5 the timed region still includes the ramp: about 8% lower).
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the headline one); the general-forward workloads "
                          "(decode_32k, chunk_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
@@ -83,6 +87,71 @@ def cpu_baseline(w, inp, causal, budget_s):
         "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the same workload, full N x N each, "
                   f"fp64 numpy, {dt:.1f} s; flops credited as for the GPU",
     }
+
+
+def timing_trials(fn, stream, trials=20, per=10):
+    """Per-launch time over `trials` runs of `per` back-to-back launches
+    (HIP events on the launch stream): median and minimum, in ms."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(trials):
+        e0.record(stream)
+        for _ in range(per):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / per)
+    times.sort()
+    return {"trials": trials, "launches_per_trial": per, "median_ms": round(times[len(times) // 2], 5),
+            "min_ms": round(times[0], 5)}
+
+
+def gpu_metrics_under_load(fn, stream, samples=3):
+    """GPU clock and socket power read by `amd-smi` (a child process, queried
+    `samples` times one after the other) while the kernel runs back to back
+    (the queue is kept about 100 launches deep); None when amd-smi is
+    unavailable or its output cannot be read."""
+    import subprocess
+
+    def query():
+        try:
+            return subprocess.Popen(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], stdout=subprocess.PIPE,
+                                    stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            return None
+
+    def parse(out):
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_") and isinstance(v, dict)
+                and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+        return (sum(clks) / len(clks) if clks else None), g["power"]["socket_power"]["value"]
+
+    for _ in range(200):  # ramp the clock before the first query
+        fn()
+    got, n, t0 = [], 0, time.perf_counter()
+    proc = query()
+    if proc is None:
+        return None
+    while len(got) < samples and time.perf_counter() - t0 < 60:
+        for _ in range(100):
+            fn()
+        n += 100
+        if proc.poll() is not None:
+            try:
+                got.append(parse(proc.communicate(timeout=30)[0]))
+            except Exception:  # format differences between amd-smi versions: report nothing rather than guess
+                return None
+            if len(got) < samples:
+                proc = query()
+        stream.synchronize()
+    stream.synchronize()
+    if not got:
+        return None
+    clks = [c for c, _ in got if c is not None]
+    return {"source": f"amd-smi metric -c -p, {len(got)} queries during back-to-back launches", "launches": n,
+            "gfx_clk_mhz": [round(c, 1) for c in clks], "socket_power_w": [p for _, p in got]}
 
 
 def main():
@@ -175,6 +244,9 @@ def main():
         },
         "wall_s_timed_region": round(wall_s, 4),
     }
+    step = lambda: fwd(q, k, v, o, lse, w.scale, causal)  # noqa: E731
+    result["timing"] = timing_trials(step, stream)
+    result["gpu"] = gpu_metrics_under_load(step, stream)
 
     if not args.no_backward and inp.do is not None:
         do = torch.from_numpy(inp.do).to(tdt).to(dev)
