@@ -78,14 +78,17 @@ def cpu_baseline(w, inp, causal, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    per_head = w.fwd_flops(causal) / (w.B * w.Hq)
+    if w.bound == "hbm":  # same unit as the GPU line: the slices' share of the minimum traffic per second
+        per_head, scale_to, unit, what = w.min_fwd_bytes() / (w.B * w.Hq), 1e9, "GB/s", "minimum bytes"
+    else:
+        per_head, scale_to, unit, what = w.fwd_flops(causal) / (w.B * w.Hq), 1e12, "TFLOP/s", "flops"
     return {
-        "value": round(per_head * heads / dt / 1e12, 6),
-        "unit": "TFLOP/s",
+        "value": round(per_head * heads / dt / scale_to, 6),
+        "unit": unit,
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the same workload, full N x N each, "
-                  f"fp64 numpy, {dt:.1f} s; flops credited as for the GPU",
+                  f"fp64 numpy, {dt:.1f} s; {what} credited as for the GPU",
     }
 
 
@@ -213,10 +216,27 @@ def main():
 
     traffic = _stored_traffic(args.traffic_file or os.path.join(ROOT, "profiles", f"fwd_bf16_{w.name}.md"))
 
+    nbytes = w.min_fwd_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kernel = (f"fwd_bf16_kernel<{w.d},64,{8 if w.d <= 128 else 4},{'true' if causal else 'false'}>"
+              if w.dtype == "bf16" else f"fwd_kernel<float,{w.d}>")
+    mask = "causal" if causal else "non-causal"
+    if w.bound == "hbm":
+        # Short sequences: the line is the minimum traffic (read Q, K, V; write
+        # O, lse once) over the time, against the HBM peak.
+        metric, value, unit = f"attention fwd HBM GB/s ({w.dtype}, {mask}, short sequences)", round(gbs, 3), "GB/s"
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "min_hbm_bytes": nbytes}
+    else:
+        metric, value, unit = (f"attention fwd TFLOP/s ({w.dtype}, {mask}) and % of MI355X bf16 MFMA peak",
+                               round(tflops, 3), "TFLOP/s")
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "min_hbm_bytes": nbytes}
     result = {
-        "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
+        "metric": metric,
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -230,18 +250,10 @@ def main():
             "workload": w.name,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": causal,
             "storage": w.dtype, "accumulate": "fp32", "seed": w.seed, "heavy_rows_frac": w.heavy_frac,
-            "credited_flops": flops, "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "credited_flops": flops, "tflops": round(tflops, 3),
+            "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "fwd_bf16_kernel<128,64,8,causal>",
-            "achieved": round(tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "min_hbm_bytes": w.min_fwd_bytes(),
-        },
+        "roofline": roofline,
         "wall_s_timed_region": round(wall_s, 4),
     }
     step = lambda: fwd(q, k, v, o, lse, w.scale, causal)  # noqa: E731

@@ -25,6 +25,7 @@ class Workload:
     heavy_frac: float = 0.0
     backward: bool = False
     note: str = ""
+    bound: str = "mfma"  # what limits the forward at this shape: "mfma" or "hbm" (short sequences)
 
     @property
     def scale(self) -> float:
@@ -62,6 +63,12 @@ WORKLOADS = {
         Workload("gqa_4k", 2, 32, 8, 4096, 128, "bf16", (True,), 3),
         Workload("wide_4k", 2, 16, 16, 4096, 256, "bf16", (False,), 3),
         Workload("bwd_4k", 2, 16, 16, 4096, 128, "bf16", (True,), 4, backward=True),
+        # Short sequences: N/2 flop per byte, below the MI355X ridge (about 315
+        # flop/B), so the forward is bound by HBM bandwidth there.
+        Workload("short_256", 16, 32, 32, 256, 128, "bf16", (False,), 5, bound="hbm",
+                 note="HBM-bound line: minimum traffic Q+K+V+O+lse over time"),
+        Workload("short_512", 16, 32, 32, 512, 128, "bf16", (False,), 5, bound="hbm",
+                 note="HBM-bound line: minimum traffic Q+K+V+O+lse over time"),
     ]
 }
 

@@ -84,7 +84,7 @@ def test_fwd_scale_zero_uniform():
     assert np.max(np.abs(from_dev(lse) - np.log(cnt)[None, None])) <= 1e-5 * math.log(200)
 
 
-FULL = [(n, c) for n in ("fwd_2k", "long_8k", "long_16k", "gqa_4k", "wide_4k", "bwd_4k")
+FULL = [(n, c) for n in ("fwd_2k", "long_8k", "long_16k", "gqa_4k", "wide_4k", "bwd_4k", "short_256", "short_512")
         for c in WORKLOADS[n].causal]
 
 
