@@ -10,7 +10,8 @@ fp32 accumulation, 1% of query rows scaled x8, seed 2.
 
 Prints ONE JSON line: throughput in TFLOP/s (credited flops 4*B*Hq*N^2*d,
 halved when causal), the roofline of the forward kernel (MFMA-bound, against
-the 2.5 PFLOP/s dense bf16 peak), the per-launch median and minimum over 20
+the 2.5 PFLOP/s dense bf16 peak and against the rate a back-to-back MFMA
+probe reaches on the same GPU), the per-launch median and minimum over 20
 trials of 10 launches, the GPU clock and power read by amd-smi under load,
 the backward pass measured the same way, the three-pass materialising
 baseline on the same inputs, and the CPU oracle timed on a bounded sample of
@@ -90,6 +91,31 @@ def cpu_baseline(w, inp, causal, budget_s):
         "sample": f"{heads} of {w.B * w.Hq} (batch, head) slices of the same workload, full N x N each, "
                   f"fp64 numpy, {dt:.1f} s; {what} credited as for the GPU",
     }
+
+
+def measured_mfma_peak(stream, iters=80000, blocks=1024):
+    """TFLOP/s of back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD (the
+    probe library built beside the attention library), one timed launch of
+    about 20 ms after an untimed one; None when the probe is not built."""
+    import ctypes
+    import torch
+    from online_softmax_flash_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    if lib.fa_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), iters, blocks, sh) != 0:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    lib.fa_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), iters, blocks, sh)
+    e1.record(stream)
+    e1.synchronize()
+    flops = blocks * 4 * 4 * iters * 2.0 * 32 * 32 * 16
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def timing_trials(fn, stream, trials=20, per=10):
@@ -259,6 +285,14 @@ def main():
     step = lambda: fwd(q, k, v, o, lse, w.scale, causal)  # noqa: E731
     result["timing"] = timing_trials(step, stream)
     result["gpu"] = gpu_metrics_under_load(step, stream)
+    if roofline["bound"] == "mfma":
+        mp = measured_mfma_peak(stream)
+        if mp:
+            roofline["measured_peak"] = round(mp, 1)
+            roofline["frac_of_measured_peak"] = round(tflops / mp, 4)
+            # One 32x32x16 bf16 product per 32 cycles per SIMD, 1024 SIMDs:
+            # the clock the probe ran at.
+            roofline["probe_clock_ghz"] = round(mp * 1e12 / (1024 * 1024 * 32768 / 32) / 1e9, 3)
 
     if not args.no_backward and inp.do is not None:
         do = torch.from_numpy(inp.do).to(tdt).to(dev)

@@ -3,6 +3,8 @@
 Usage: ``python -m online_softmax_flash_amd.build`` (or ``build()`` from Python).
 Every source under ``csrc/`` is compiled to an object in ``_build/`` (in
 parallel), then linked into ``online_softmax_flash_amd/libflashattn.so``.
+``probe/mfma_peak.hip`` becomes ``libfaprobe.so``, the benchmark's
+matrix-core throughput probe.
 """
 
 from __future__ import annotations
@@ -19,6 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflashattn.so")
+# Matrix-core throughput probe for the benchmark's roofline (not the library).
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
+PROBE_LIB = os.path.join(PKG, "libfaprobe.so")
 ARCH = "gfx950"
 
 # No packed fp32 arithmetic (v_pk_*_f32) in device code.
@@ -68,6 +73,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
