@@ -197,6 +197,10 @@ struct LeanDma {
 
 template <int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
+  // Persistent workgroups (several items each) up to d = 128; at d = 256 (one
+  // wave per SIMD, most registers in use) one item per workgroup measured
+  // faster, and the item loop compiles away.
+  constexpr bool PERSIST = D <= 128;
   using C = Bf16FwdCfg<D, BN, NW>;
   constexpr int BM = C::BM;
   constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
@@ -208,33 +212,46 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, li = lane & 31;
   const int nqb = (N + BM - 1) / BM;
-  int b, hq, qb;
-  decode_block(blockIdx.x, a.Hq, a.B, nqb, CAUSAL, b, hq, qb);
-  const int hkv = hq / (a.Hq / a.Hkv);
-  const int q0 = qb * BM;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + li;
-
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (size_t)(b * a.Hq + hq) * N * D;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + hkv) * N * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + hkv) * N * D;
-
   const int nkb = (N + BN - 1) / BN;
-  const int q_last = min(q0 + BM, N) - 1;
-  const int kb_end = CAUSAL ? min(nkb, q_last / BN + 1) : nkb;
-  // Blocks [0, kb_full) need no mask for any query of the workgroup: every key
-  // is < N and (causal) <= the first query q0.
-  const int kb_full = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+  const int nfull_rows = N / BN;  // blocks with all BN rows inside [0, N)
+
+  // Work items (query block, head, batch), longest first (decode_block). The
+  // grid holds one workgroup per CU; workgroup w takes items w, then in every
+  // other round the mirror image of w among the workgroups of its XCD, so
+  // that long and short items pair up (balanced causal work) and every item
+  // runs on the XCD the head order assigns it (L2 reuse of K and V).
+  const int G = (int)gridDim.x, n_items = nqb * a.Hq * a.B;
+  auto item_of = [&](int r) {
+    const int w = (int)blockIdx.x;
+    const int ww = ((r & 1) && G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + w % 8 : w;
+    return r * G + ww;
+  };
+  struct Item {
+    int b, hq, q0, kb_end, kb_full;
+  };
+  auto make_item = [&](int it) {
+    Item x;
+    int qb;
+    decode_block(it, a.Hq, a.B, nqb, CAUSAL, x.b, x.hq, qb);
+    x.q0 = qb * BM;
+    const int q_last = min(x.q0 + BM, N) - 1;
+    x.kb_end = CAUSAL ? min(nkb, q_last / BN + 1) : nkb;
+    // Blocks [0, kb_full) need no mask for any query of the workgroup: every
+    // key is < N and (causal) <= the first query q0.
+    x.kb_full = CAUSAL ? min((x.q0 + 1) / BN, N / BN) : N / BN;
+    return x;
+  };
 
   BlockDma<D, BN, C::KROW, NW> kdma;
   BlockDma<D, BN, C::VROW, NW> vdma;
   kdma.init(wave, lane);
   vdma.init(wave, lane);
-  const int nfull_rows = N / BN;  // blocks with all BN rows inside [0, N)
-  auto prefetch = [&](int kb) {
-    uint8_t* st = smem + (kb & 1) * STAGE;
-    const uint16_t* kg = K + (size_t)kb * BN * D;
-    const uint16_t* vg = V + (size_t)kb * BN * D;
+  // Block kb of item x into LDS stage st (0 or 1).
+  auto copy_block = [&](const Item& x, int kb, int st_idx) {
+    uint8_t* st = smem + st_idx * STAGE;
+    const size_t off = ((size_t)(x.b * a.Hkv + x.hq / (a.Hq / a.Hkv)) * N + (size_t)kb * BN) * D;
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k) + off;
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v) + off;
     if (kb < nfull_rows) {
       kdma.template issue<true>(st, kg, BN, wave);
       vdma.template issue<true>(st + C::KBYTES, vg, BN, wave);
@@ -243,20 +260,38 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
       vdma.template issue<false>(st + C::KBYTES, vg, N - kb * BN, wave);
     }
   };
-  prefetch(0);  // in flight while the query rows are read
-
   bf16x8 qf[NF];
+  auto load_q = [&](const Item& x) {
+    const int q = x.q0 + wave * 32 + li;
+    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + (size_t)(x.b * a.Hq + x.hq) * N * D;
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
-    qf[f] = (qi < N) ? global_frag<uint16_t>(Q + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    for (int f = 0; f < NF; ++f)
+      qf[f] = (q < N) ? global_frag<uint16_t>(Q + (size_t)q * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+  };
+
+  int round = 0;
+  Item cur = make_item(item_of(0));  // the grid never exceeds the item count
+  int base = 0;                      // blocks of earlier items: block kb of this item uses stage (base + kb) & 1
+  copy_block(cur, 0, 0);             // in flight while the query rows are read
+  load_q(cur);
 
   f32x16 oacc[NDT];
+  float m_run, l_bf, l_32;
+  const float c = a.c;
+  for (;;) {
+  const int q0 = cur.q0;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + li;
+  const int kb_end = cur.kb_end, kb_full = cur.kb_full;
+  const int next_item = item_of(round + 1);
+  const bool has_next = PERSIST && next_item < n_items;
+  auto prefetch = [&](int kb) { copy_block(cur, kb, (base + kb) & 1); };
+
 #pragma unroll
   for (int t = 0; t < NDT; ++t) oacc[t] = zero16();
-  float m_run = -INFINITY;  // reference maximum of s*c (log2 units)
-  float l_bf = 0.f;         // this lane's share of sum of the bf16-rounded weights (normalises O)
-  float l_32 = 0.f;         // this lane's share of sum of the fp32 weights (gives lse)
-  const float c = a.c;
+  m_run = -INFINITY;  // reference maximum of s*c (log2 units)
+  l_bf = 0.f;         // this lane's share of sum of the bf16-rounded weights (normalises O)
+  l_32 = 0.f;         // this lane's share of sum of the fp32 weights (gives lse)
 
   // Per-lane byte offsets of the fragment reads.
   // K (A operand of S^T): row 32*kt + sigma(li), bytes 32*f + 16*h.
@@ -267,11 +302,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   const int v_off = C::KBYTES + (8 * h + (i16 >> 2)) * C::VROW + 2 * (16 * (g16 & 1) + 4 * (i16 & 3));
 
   // One key block: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
-  auto block = [&](int kb, auto masked_tag) {
+  // after_scores() runs once the score products are issued (at once when the
+  // wave skips the block): in the item's last block it reads the next item's
+  // query rows, whose registers the products no longer need.
+  auto block = [&](int kb, auto masked_tag, auto&& after_scores) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = kb * BN;
-    if (CAUSAL && k0 > qw0 + 31) return;  // every key of the block follows every query of this wave
-    const uint8_t* st = smem + (kb & 1) * STAGE;
+    if (CAUSAL && k0 > qw0 + 31) {  // every key of the block follows every query of this wave
+      after_scores();
+      return;
+    }
+    const uint8_t* st = smem + ((base + kb) & 1) * STAGE;
     f32x16 s[NKT];
     {
       bf16x8 kf[NKT][NF];
@@ -298,6 +339,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
       }
     }
+    after_scores();
     bool keep[NKT][16];
     if constexpr (MASKED) {
 #pragma unroll
@@ -382,18 +424,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     });
   };
 
+  // After the barrier of block kb: the copy of block kb+1, or, in the last
+  // block, of the next item's first block (into the stage just freed).
+  auto after_barrier = [&](int kb) {
+    if (kb + 1 < kb_end) prefetch(kb + 1);
+    else if (has_next) copy_block(make_item(next_item), 0, (base + kb_end) & 1);
+  };
+  auto after_scores = [&](int kb) {
+    if (kb + 1 == kb_end && has_next) load_q(make_item(next_item));
+  };
   int kb = 0;
   for (; kb < kb_full; ++kb) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // block kb has landed; every wave is done with block kb-1
-    if (kb + 1 < kb_end) prefetch(kb + 1);
-    block(kb, std::false_type{});
+    after_barrier(kb);
+    block(kb, std::false_type{}, [&] { after_scores(kb); });
   }
   for (; kb < kb_end; ++kb) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kb + 1 < kb_end) prefetch(kb + 1);
-    block(kb, std::true_type{});
+    after_barrier(kb);
+    block(kb, std::true_type{}, [&] { after_scores(kb); });
   }
 
   // Epilogue: divide by the denominator once; lse in natural-log units.
@@ -401,7 +452,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   const float l32 = l_32 + __shfl_xor(l_32, 32);
   const float inv = 1.f / lb;
   if (qi < N) {
-    uint16_t* O = static_cast<uint16_t*>(a.o) + (size_t)(b * a.Hq + hq) * N * D + (size_t)qi * D;
+    uint16_t* O = static_cast<uint16_t*>(a.o) + (size_t)(cur.b * a.Hq + cur.hq) * N * D + (size_t)qi * D;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
@@ -411,16 +462,35 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) to_elem(oacc[t][4 * g + e] * inv, out[e]);
         *reinterpret_cast<uint2*>(O + 32 * t + 8 * g + 4 * h) = *reinterpret_cast<const uint2*>(out);
       }
-    if (h == 0) a.lse[(size_t)(b * a.Hq + hq) * N + qi] = (m_run + __log2f(l32)) * 0.69314718055994531f;
+    if (h == 0) a.lse[(size_t)(cur.b * a.Hq + cur.hq) * N + qi] = (m_run + __log2f(l32)) * 0.69314718055994531f;
   }
+  if (!has_next) break;
+  base += kb_end;
+  cur = make_item(next_item);
+  ++round;
+  }
+}
+
+// Compute units of the current device (cached per device).
+inline int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int D, int BN, int NW, bool CAUSAL>
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * NW;
-  const int nqb = (a.N + BM - 1) / BM;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NW), 0,
-                     stream, a);
+  const long long items = (long long)((a.N + BM - 1) / BM) * a.Hq * a.B;
+  const long long cap = D <= 128 ? device_cu_count() : items;  // one item per workgroup at d = 256
+  const int grid = (int)(items < cap ? items : cap);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
