@@ -474,14 +474,19 @@ FWD_SOURCES = ("fa_device.hpp", "fa_fwd.hpp", "fa_fwd_bf16.hpp", "fa_fwd_bf16.hi
 
 
 def _kernel_sha() -> str:
-    """Hash of the headline forward's sources and flags, to tell whether stored counter data is current."""
+    """Hash of the headline forward's sources (comments and layout left out:
+    only code counts) and build flags, to tell whether stored counter data is
+    current."""
     import hashlib
+    import re
     from online_softmax_flash_amd import build as b
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "online_softmax_flash_amd", "csrc")
     for f in FWD_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(f.encode() + " ".join(code.split()).encode())
     flags = b.COMMON + b.DEVICE_FLAGS + b.EXTRA_FLAGS.get("fa_fwd_bf16.hip", [])
     h.update(repr([f.replace(b.ROOT, "<root>") for f in flags]).encode())  # independent of where the tree lives
     return h.hexdigest()[:16]

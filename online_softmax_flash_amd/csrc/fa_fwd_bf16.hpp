@@ -24,6 +24,11 @@
 //    arithmetic: numerator and denominator always share the same reference.
 //  * Causal: a wave whose 32 queries all precede a block skips its compute
 //    (it still takes part in the block's loads and barrier).
+//  * Persistent workgroups (d <= 128): one per CU, each running several work
+//    items (query block, head, batch). During an item's last block the next
+//    item's first K/V block and query rows are already loaded, so an item's
+//    start-up latency hides behind the previous item's work (this matters
+//    most for short sequences, with few blocks per item).
 #pragma once
 
 #include <type_traits>
