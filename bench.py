@@ -292,7 +292,7 @@ def main():
             roofline["frac_of_measured_peak"] = round(tflops / mp, 4)
             # One 32x32x16 bf16 product per 32 cycles per SIMD, 1024 SIMDs:
             # the clock the probe ran at.
-            roofline["probe_clock_ghz"] = round(mp * 1e12 / (1024 * 1024 * 32768 / 32) / 1e9, 3)
+            roofline["probe_clock_ghz"] = round(mp * 1e12 / (1024 * 32768 / 32) / 1e9, 3)
 
     if not args.no_backward and inp.do is not None:
         do = torch.from_numpy(inp.do).to(tdt).to(dev)
