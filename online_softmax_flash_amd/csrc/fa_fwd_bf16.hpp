@@ -22,6 +22,11 @@
 //    so exponentials are at most 2^TAU and the O rescale (and its VALU work)
 //    is skipped for most blocks. The final o / l is unchanged in exact
 //    arithmetic: numerator and denominator always share the same reference.
+//    Only an item's first block (and masked blocks) take the block maximum;
+//    other blocks take the weights against the current reference directly
+//    and check their sum (the rare block whose maximum jumped is computed
+//    again), so the second score tile's products overlap the first tile's
+//    exponentials.
 //  * Causal: a wave whose 32 queries all precede a block skips its compute
 //    (it still takes part in the block's loads and barrier).
 //  * Persistent workgroups (d <= 128): one per CU, each running several work
@@ -210,6 +215,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BM = C::BM;
   constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
   constexpr float TAU = 8.0f;
+  constexpr float kTwoPowTau = 256.0f;  // 2^TAU
   constexpr int STAGE = C::KBYTES + C::VBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     }
     const uint8_t* st = smem + ((base + kb) & 1) * STAGE;
     f32x16 s[NKT];
-    {
+    auto scores = [&] {
       bf16x8 kf[NKT][NF];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -331,9 +337,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
       }
-      // Schedule (d <= 128): the first tile's K reads, then each later read
-      // paired with one product, then the remaining products -- reads run
-      // ahead of use. At d = 256 the registers for that are not there.
       if constexpr (D <= 128) {
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
@@ -343,30 +346,92 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
       }
-    }
-    after_scores();
+    };
     bool keep[NKT][16];
-    if constexpr (MASKED) {
+    auto mask = [&] {
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kt + sigma_row(r, h);
+            keep[kt][r] = key < N && (!CAUSAL || key <= qi);
+            if (!keep[kt][r]) s[kt][r] = -INFINITY;
+          }
+      }
+    };
+    // Raise the reference maximum if the block's maximum exceeds it by more
+    // than TAU; returns the factor by which o and l must be rescaled (1: none).
+    auto raise_max = [&] {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
+      float alpha = 1.f;
+      if (__any(mxc > m_run + TAU)) {
+        const float m_new = fmaxf(m_run, mxc);
+        alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      }
+      return alpha;
+    };
+    // Weights exp2(s*c - m_run) in place; returns this lane's fp32 sum of them.
+    auto weights = [&] {
+      const float base = (m_run == -INFINITY) ? 0.f : m_run;
+      float p32[2] = {0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kt + sigma_row(r, h);
-          keep[kt][r] = key < N && (!CAUSAL || key <= qi);
-          if (!keep[kt][r]) s[kt][r] = -INFINITY;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -base));
+          if constexpr (MASKED) p = keep[kt][r] ? p : 0.f;
+          s[kt][r] = p;
+          p32[r & 1] += p;
         }
+      return p32[0] + p32[1];
+    };
+    // The item's first block sets the reference maximum. Later unmasked
+    // blocks take the weights against the current reference first: every
+    // weight is at most the lane's sum, so a sum <= 2^TAU shows that no score
+    // exceeded the reference by more than TAU (the condition for raising it).
+    // Otherwise (rare: the maximum jumped; an overflowed weight gives an
+    // infinite sum) the block's scores are computed again and the reference
+    // raised first, which is the decision the block maximum would have taken:
+    // the results are those of taking the maximum in every block.
+    float psum, alpha = 1.f;
+    bool slow = (kb == 0) || MASKED;
+    if (!slow) {
+      // Unmasked later block: the products of the second score tile run
+      // while the weights of the first are taken.
+      scores();
+      psum = weights();
+      if constexpr (D <= 128) {
+        // K reads, then tile 0's products, then tile 1's products each
+        // followed by a share of tile 0's weight arithmetic.
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 1);
+        for (int i = 0; i < (NKT - 1) * NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        }
+        for (int i = 0; i < NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+        }
+      }
+      slow = __any(!(psum <= kTwoPowTau));
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (__any(mxc > m_run + TAU)) {
-      const float m_new = fmaxf(m_run, mxc);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    if (slow) {
+      asm volatile("" ::: "memory");  // read K again (the first reads are not kept live)
+      scores();
+      mask();
+      alpha = raise_max();
+      psum = weights();
+    }
+    after_scores();
+    if (__any(alpha != 1.f)) {
       l_bf *= alpha;
       l_32 *= alpha;
 #pragma unroll
@@ -374,18 +439,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
     }
-    const float base = (m_run == -INFINITY) ? 0.f : m_run;
-    float p32[2] = {0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -base));
-        if constexpr (MASKED) p = keep[kt][r] ? p : 0.f;
-        s[kt][r] = p;
-        p32[r & 1] += p;
-      }
-    l_32 += p32[0] + p32[1];
+    l_32 += psum;
     // P rounded to bf16 (the B operand of P V). O is normalised by the sum of
     // these same rounded weights (v_dot2 against (1, 1)), so o / l is an exact
     // convex combination of the weights the matrix cores used.

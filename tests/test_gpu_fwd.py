@@ -154,3 +154,31 @@ def test_fwd_very_long_single_head(d):
         O_ref, L_ref = oracle.attn_fwd_head(inp.q[0, 0], inp.k[0, 0], inp.v[0, 0], scale, causal, rows=rows)
         assert_close(o_h[0, 0, rows], O_ref, "bf16", f"N={N} d={d} causal={causal} O")
         assert_close(lse_h[0, 0, rows], L_ref, "bf16", f"N={N} d={d} causal={causal} lse", lse=True)
+
+
+@pytest.mark.parametrize("case", ["jump", "overflow"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fwd_late_maximum_jump(d, case):
+    """Running maximum that jumps in a later, unmasked key block. Key 150 (the
+    third 64-key block) is set to alpha * q_900, so query 900 and the rows
+    whose queries align with it score far above everything in the first two
+    blocks: by about 8 to 17 (alpha = 1) and by 170 to 240 (alpha = 16, or 8
+    at d = 256) in log2 units, where a weight taken against the earlier
+    maximum would overflow fp32. The kernels must raise their reference
+    maximum as the block maximum dictates; compared element by element
+    against the oracle, both masks."""
+    alpha = 1.0 if case == "jump" else (16.0 if d <= 128 else 8.0)
+    B, H, N = 1, 2, 1024
+    announce(f"fwd late max jump d={d} alpha={alpha} seed=71")
+    inp = make_inputs(B, H, H, N, d, seed=71)
+    k = inp.k.copy()
+    k[:, :, 150, :] = alpha * inp.q[:, :, 900, :]  # power-of-two multiple of bf16 values: exact
+    scale = 1.0 / math.sqrt(d)
+    q_d, k_d, v_d = (to_dev(x, "bf16") for x in (inp.q, k, inp.v))
+    for causal in (False, True):
+        o, lse = fa.attention_forward(q_d, k_d, v_d, scale, causal)
+        torch.cuda.synchronize()
+        O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, k, inp.v, scale, causal)
+        assert np.abs(L_ref[:, :, 900]).min() > (100.0 if alpha > 1 else 5.0)
+        assert_close(from_dev(o), O_ref, "bf16", f"O d={d} alpha={alpha} causal={causal}")
+        assert_close(from_dev(lse), L_ref, "bf16", f"lse d={d} alpha={alpha} causal={causal}", lse=True)
