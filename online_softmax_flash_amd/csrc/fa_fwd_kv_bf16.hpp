@@ -40,6 +40,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   constexpr int BM = C::BM;
   constexpr int NF = D / 16, NKT = BN / 32, NDT = D / 32, NKC = BN / 16;
   constexpr float TAU = 8.0f;
+  constexpr float kTwoPowTau = 256.0f;  // 2^TAU
   constexpr int STAGE = C::KBYTES + C::VBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
     if (CAUSAL && k0 > wave_kmax) return;
     const uint8_t* st = smem + (kb & 1) * STAGE;
     f32x16 s[NKT];
-    {
+    auto scores = [&] {
       bf16x8 kf[NKT][NF];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -146,7 +147,83 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
       }
-      // The first tile's K reads, then each later read beside one product.
+    };
+    bool keep[NKT][16];
+    auto mask = [&] {
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            keep[kt][e] = k0 + 32 * kt + sigma_row(e, h) <= klim;
+            if (!keep[kt][e]) s[kt][e] = -INFINITY;
+          }
+      }
+    };
+    // Raise the reference maximum if the block's maximum exceeds it by more
+    // than TAU; returns the factor by which o and l must be rescaled (1: none).
+    auto raise_max = [&] {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
+      float alpha = 1.f;
+      if (__any(mxc > m_run + TAU)) {
+        const float m_new = fmaxf(m_run, mxc);
+        alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+      }
+      return alpha;
+    };
+    // Weights exp2(s*c - m_run) in place; returns this lane's fp32 sum of them.
+    auto weights = [&] {
+      const float base = (m_run == -INFINITY) ? 0.f : m_run;
+      float p32[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], c, -base));
+          if constexpr (MASKED) p = keep[kt][e] ? p : 0.f;
+          s[kt][e] = p;
+          p32[e & 1] += p;
+        }
+      return p32[0] + p32[1];
+    };
+    // The first block of the key range sets the reference maximum; masked
+    // blocks take the block maximum too. Other blocks (every key visible to
+    // every row, and every row already holds a finite reference, since the
+    // visible keys of a row are a prefix) take the weights against the
+    // current reference first: a lane sum <= 2^TAU shows that no score
+    // exceeded the reference by more than TAU. Otherwise (rare) the scores
+    // are computed again and the reference raised first, the decision the
+    // block maximum would have taken.
+    float psum, alpha = 1.f;
+    bool slow = (kb == kb0) || MASKED;
+    if (!slow) {
+      scores();
+      psum = weights();
+      if constexpr (D <= 128) {
+        // K reads, then tile 0's products, then the later tiles' products
+        // each followed by a share of the weight arithmetic.
+        __builtin_amdgcn_sched_group_barrier(0x100, NF, 1);
+        for (int i = 0; i < (NKT - 1) * NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        }
+        for (int i = 0; i < NF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+        }
+      }
+      slow = __any(!(psum <= kTwoPowTau));
+    }
+    if (slow) {
+      asm volatile("" ::: "memory");  // read K again (the first reads are not kept live)
+      scores();
       if constexpr (D <= 128) {
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
@@ -156,28 +233,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
       }
+      mask();
+      alpha = raise_max();
+      psum = weights();
     }
-    bool keep[NKT][16];
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          keep[kt][e] = k0 + 32 * kt + sigma_row(e, h) <= klim;
-          if (!keep[kt][e]) s[kt][e] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxc = (mx == -INFINITY) ? -INFINITY : mx * c;
-    if (__any(mxc > m_run + TAU)) {
-      const float m_new = fmaxf(m_run, mxc);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    if (__any(alpha != 1.f)) {
       l_bf *= alpha;
       l_32 *= alpha;
 #pragma unroll
@@ -185,18 +245,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
     }
-    const float base = (m_run == -INFINITY) ? 0.f : m_run;
-    float p32[2] = {0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], c, -base));
-        if constexpr (MASKED) p = keep[kt][e] ? p : 0.f;
-        s[kt][e] = p;
-        p32[e & 1] += p;
-      }
-    l_32 += p32[0] + p32[1];
+    l_32 += psum;
     uint32_t pw[NKC][4];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
