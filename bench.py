@@ -139,8 +139,8 @@ def timing_trials(fn, stream, trials=20, per=10):
 def gpu_metrics_under_load(fn, stream, samples=3):
     """GPU clock and socket power read by `amd-smi` (a child process, queried
     `samples` times one after the other) while the kernel runs back to back
-    (the queue is kept about 100 launches deep); None when amd-smi is
-    unavailable or its output cannot be read."""
+    (batches of 100 launches), after 2 s of the same load; None when amd-smi
+    is unavailable or its output cannot be read."""
     import subprocess
 
     def query():
@@ -157,24 +157,30 @@ def gpu_metrics_under_load(fn, stream, samples=3):
                 and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
         return (sum(clks) / len(clks) if clks else None), g["power"]["socket_power"]["value"]
 
-    for _ in range(200):  # ramp the clock before the first query
-        fn()
-    got, n, t0 = [], 0, time.perf_counter()
-    proc = query()
-    if proc is None:
-        return None
-    while len(got) < samples and time.perf_counter() - t0 < 60:
+    # The driver's metrics lag the load by up to about a second: keep the
+    # kernel running back to back for 2 s before the first query and for at
+    # least 0.5 s around each query.
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 2.0:
         for _ in range(100):
             fn()
         n += 100
-        if proc.poll() is not None:
-            try:
-                got.append(parse(proc.communicate(timeout=30)[0]))
-            except Exception:  # format differences between amd-smi versions: report nothing rather than guess
-                return None
-            if len(got) < samples:
-                proc = query()
         stream.synchronize()
+    got = []
+    for _ in range(samples):
+        proc = query()
+        if proc is None:
+            return None
+        tq = time.perf_counter()
+        while (proc.poll() is None or time.perf_counter() - tq < 0.5) and time.perf_counter() - tq < 30:
+            for _ in range(100):
+                fn()
+            n += 100
+            stream.synchronize()
+        try:
+            got.append(parse(proc.communicate(timeout=30)[0]))
+        except Exception:  # format differences between amd-smi versions: report nothing rather than guess
+            return None
     stream.synchronize()
     if not got:
         return None
