@@ -287,7 +287,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int N = a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Wave index in a scalar register: the per-wave tests below (causal skip,
+  // masked subtile) are then branches, not per-lane predication.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int nqb = (N + BM - 1) / BM;
