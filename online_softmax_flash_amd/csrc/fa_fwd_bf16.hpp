@@ -337,6 +337,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
       }
+      // Schedule (d <= 128): the first tile's K reads, then each later read
+      // paired with one product, then the remaining products -- reads run
+      // ahead of use. At d = 256 the registers for that are not there.
       if constexpr (D <= 128) {
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
