@@ -48,6 +48,8 @@ def parse():
                     help="workload name (default: the headline one); the general-forward workloads "
                          "(decode_32k, chunk_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock and power sampling (seconds of extra launches; for profiler runs)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip the three-pass materialising baseline timed on the same inputs")
@@ -290,7 +292,8 @@ def main():
     }
     step = lambda: fwd(q, k, v, o, lse, w.scale, causal)  # noqa: E731
     result["timing"] = timing_trials(step, stream)
-    result["gpu"] = gpu_metrics_under_load(step, stream)
+    if not args.no_clock:
+        result["gpu"] = gpu_metrics_under_load(step, stream)
     if roofline["bound"] == "mfma":
         mp = measured_mfma_peak(stream)
         if mp:

@@ -132,44 +132,47 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, uint64_t
 // into an LDS block with ROWB-byte rows (2*D data bytes + padding). The block
 // is a sequence of 16-byte slots; wave-instruction n fills slots
 // [64n, 64n + 64), lane i slot 64n + i, and this wave issues instructions
-// n = wave, wave + NW, ... Slots in the padding are skipped (lane inactive).
+// n = wave, wave + NW, ... (the wave index is made scalar here, so these
+// tests are branches); a lane whose slot is padding copies a data chunk of
+// its row again, so no instruction needs a per-lane mask.
 template <int D, int BN, int ROWB, int NW>
 struct BlockDma {
   static constexpr int SPR = ROWB / 16;   // slots per row
   static constexpr int CPR = 2 * D / 16;  // data slots per row
   static constexpr int NINSTR = (BN * SPR + 63) / 64;
   static constexpr int NPER = (NINSTR + NW - 1) / NW;  // instructions per wave (upper bound)
-  int off[NPER];  // element offset of this lane's chunk within the block, or -1
-  int row[NPER];  // its row, for clamping the ragged tail
+  static_assert(BN * SPR % 64 == 0, "every copy instruction covers 64 slots of the block");
+  // Byte offset of this lane's chunk within the block. A lane whose slot is
+  // row padding copies the row's last data chunk again (the padding is never
+  // read), so every lane of an instruction is active.
+  uint32_t off[NPER];
+  int row[NPER];  // the chunk's row, for clamping the ragged tail
 
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < NPER; ++j) {
       const int n = wave + j * NW;
       const int slot = n * 64 + lane;
-      const int r = slot / SPR, c = slot % SPR;
-      const bool ok = n < NINSTR && r < BN && c < CPR;
-      off[j] = ok ? r * D + c * 8 : -1;
-      row[j] = ok ? r : 0;
+      const int r = slot / SPR, c = min(slot % SPR, CPR - 1);
+      off[j] = (uint32_t)(r * D + c * 8) * 2u;
+      row[j] = r;
     }
   }
   // Rows >= valid read row valid - 1 (finite data; the kernel masks those keys).
   // Issued in scalar-base form (block base address and LDS destination in
-  // scalar registers, a 32-bit per-lane byte offset), so no per-lane 64-bit
-  // address arithmetic is spent per instruction.
+  // scalar registers, a 32-bit per-lane byte offset).
   template <bool FULL>
-  __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave) const {
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave_in) const {
+    const int wave = __builtin_amdgcn_readfirstlane(wave_in);  // uniform: scalar tests and LDS bases
     const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
     const uint64_t gs = uniform_u64((uint64_t)g);
 #pragma unroll
     for (int j = 0; j < NPER; ++j) {
       const int n = wave + j * NW;
       if (j * NW + NW <= NINSTR || n < NINSTR) {  // wave-uniform
-        if (off[j] >= 0) {
-          int e = off[j];
-          if (!FULL && row[j] >= valid) e -= (row[j] - valid + 1) * D;
-          dma16(lb + (uint32_t)n * 1024u, (uint32_t)e * 2u, gs);
-        }
+        uint32_t e = off[j];
+        if (!FULL && row[j] >= valid) e -= (uint32_t)((row[j] - valid + 1) * D * 2);
+        dma16(lb + (uint32_t)n * 1024u, e, gs);
       }
     }
   }
