@@ -189,17 +189,24 @@ struct LeanDma {
   static constexpr int SPR = ROWB / 16;
   static constexpr int CPR = 2 * D / 16;
   static constexpr int NINSTR = (BN * SPR + 63) / 64;
+  // Whether the last instruction runs past the block (its lanes beyond the
+  // block's last slot must stay inactive).
+  static constexpr bool TAIL = BN * SPR % 64 != 0;
   template <bool FULL>
-  __device__ __forceinline__ static void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) {
+  __device__ __forceinline__ static void issue(uint8_t* lds, const uint16_t* g, int valid, int wave_in, int lane) {
     asm volatile("" : "+v"(lane));  // recompute below on every call
+    const int wave = __builtin_amdgcn_readfirstlane(wave_in);  // uniform: scalar tests and LDS bases
     const uint64_t gs = uniform_u64((uint64_t)g);
 #pragma unroll
     for (int n0 = 0; n0 < NINSTR; n0 += NW) {
       const int n = n0 + wave;
       if (n0 + NW <= NINSTR || n < NINSTR) {  // wave-uniform
         const int slot = n * 64 + lane;
-        const int r = slot / SPR, c = slot - r * SPR;
-        if (c < CPR && r < BN) {
+        const int r = slot / SPR;
+        // A lane whose slot is row padding copies its row's last data chunk
+        // again (the padding is never read): no per-lane mask.
+        const int c = min(slot - r * SPR, CPR - 1);
+        if (!TAIL || n < NINSTR - 1 || r < BN) {
           const int rr = (!FULL && r >= valid) ? valid - 1 : r;
           dma16(lds_addr(lds) + (uint32_t)n * 1024u, (uint32_t)(rr * D + c * 8) * 2u, gs);
         }
