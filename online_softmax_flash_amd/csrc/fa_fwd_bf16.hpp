@@ -347,10 +347,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) mma(s[kt], kf[kt][f], qf[f]);
       }
-      // Schedule (d <= 128): the first tile's K reads, then each later read
-      // paired with one product, then the remaining products -- reads run
-      // ahead of use. At d = 256 the registers for that are not there.
-      if constexpr (D <= 128) {
+      // Schedule: the first tile's K reads, then each later read paired with
+      // one product, then the remaining products -- reads run ahead of use.
+      {
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
         for (int i = 0; i < (NKT - 1) * NF; ++i) {
@@ -421,7 +420,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
       // while the weights of the first are taken.
       scores();
       psum = weights();
-      if constexpr (D <= 128) {
+      {
         // K reads, then tile 0's products, then tile 1's products each
         // followed by a share of tile 0's weight arithmetic.
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 1);
@@ -475,7 +474,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     // products of chunk kc; the reads are issued and waited for explicitly
     // (see TrReads), so the in-flight copy of the next block is never waited on.
     const uint32_t vaddr = lds_addr(st) + (uint32_t)v_off;
-    constexpr bool VPIPE = D <= 128;  // double-buffer the V fragments (registers permitting)
+    constexpr bool VPIPE = true;  // double-buffer the V fragments (at d = 256 too: 390 of 512 registers)
     TrReads<NDT> vr[VPIPE ? 2 : 1];
     vr[0].template issue<0, C::VROW>(vaddr);
     static_for<0, NKC>([&](auto kcc) {
