@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
     if (!slow) {
       scores();
       psum = weights();
-      if constexpr (D <= 128) {
+      {
         // K reads, then tile 0's products, then the later tiles' products
         // each followed by a share of the weight arithmetic.
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 1);
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
     if (slow) {
       asm volatile("" ::: "memory");  // read K again (the first reads are not kept live)
       scores();
-      if constexpr (D <= 128) {
+      {
         __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
         for (int i = 0; i < (NKT - 1) * NF; ++i) {
@@ -262,9 +262,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
         pbf[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kc][e]), kOnesBf16x2, pbf[e & 1], false);
     l_bf += pbf[0] + pbf[1];
     // V fragments of chunk kc+1 are requested before the products of chunk kc
-    // (registers permitting).
+    // (at d = 256 too: the registers fit without spills).
     const uint32_t vaddr = lds_addr(st) + (uint32_t)v_off;
-    constexpr bool VPIPE = D <= 128;
+    constexpr bool VPIPE = true;
     TrReads<NDT> vr[VPIPE ? 2 : 1];
     vr[0].template issue<0, C::VROW>(vaddr);
     static_for<0, NKC>([&](auto kcc) {

@@ -140,6 +140,8 @@ KV_WORKLOADS = {
                    note="one decode step: 8 sequences, 32 query heads on 8 K/V heads, 32768 cached keys"),
         KvWorkload("chunk_2k_8k", 1, 32, 8, 2048, 8192, 128, True, 6,
                    note="chunked prefill: the last 2048 queries of an 8192-token causal prefix"),
+        KvWorkload("chunk_wide_2k_8k", 1, 16, 16, 2048, 8192, 256, True, 9,
+                   note="chunked prefill at d = 256: the last 2048 queries of an 8192-token causal prefix"),
         KvWorkload("varlen_mix", 16, 32, 8, 4096, 4096, 128, True, 7, Nq_lo=64, Nk_lo=64, lengths_seed=8,
                    note="16 sequences, log-uniform lengths in [64, 4096], queries = keys per sequence"),
     ]

@@ -127,7 +127,7 @@ def _kv_full(name):
     return w, make_kv_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed), None
 
 
-@pytest.mark.parametrize("name", ["decode_32k", "chunk_2k_8k"])
+@pytest.mark.parametrize("name", ["decode_32k", "chunk_2k_8k", "chunk_wide_2k_8k"])
 def test_kv_full_size_sampled(name):
     w, inp, _ = _kv_full(name)
     announce(f"kv full {name} shape=({w.B},{w.Hq},{w.Hkv},{w.Nq},{w.Nk},{w.d}) seed={w.seed}")
