@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the headline one); the general-forward workloads "
-                         "(decode_32k, chunk_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
+                         "(decode_32k, chunk_2k_8k, chunk_wide_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the amd-smi clock and power sampling (seconds of extra launches; for profiler runs)")
