@@ -187,16 +187,21 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
     const uint8_t* os = st + TILE;
     const uint8_t* rows = pwave ? qs : os;
     const uint8_t* trs = pwave ? os : qs;
+    // The products of a subtile are issued even when it is not needed (its
+    // rows are in LDS either way; the result is then not used), so that in
+    // the P wave subtile 1's products and subtile 0's exponentials sit in
+    // one basic block and the scheduler can interleave them.
     f32x16 x[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    auto products = [&](int sub) {
       x[sub] = zero16();
-      if (!(sub ? need1 : need0)) continue;
 #pragma unroll
       for (int f = 0; f < NF; ++f) mma(x[sub], *reinterpret_cast<const bf16x8*>(rows + sub * 32 * RS + row_off + 32 * f), kvf[f]);
-    }
+    };
+    products(0);
     bf16x8 bfr[2][2];
+    if (!pwave) products(1);
     if (pwave) {
+      products(1);
       // P = exp2(S*c - l2) with masks; P to LDS for the dS wave; bf16 fragments.
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
