@@ -44,6 +44,9 @@ def parse():
     # Enough untimed launches for the GPU clock to leave its idle state (with
     # 5 the timed region still includes the ramp: about 8% lower).
     ap.add_argument("--warmup", type=int, default=50)
+    # Before the warmup launches: launches back to back for this long (untimed),
+    # so that the GPU clock has left its idle state whatever --warmup is.
+    ap.add_argument("--ramp-seconds", type=float, default=1.5)
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the headline one); the general-forward workloads "
                          "(decode_32k, chunk_2k_8k, chunk_wide_2k_8k, varlen_mix) time flash_attn_fwd_kv / flash_attn_fwd_varlen")
@@ -118,6 +121,20 @@ def measured_mfma_peak(stream, iters=80000, blocks=1024):
     e1.synchronize()
     flops = blocks * 4 * 4 * iters * 2.0 * 32 * 32 * 16
     return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
+def clock_ramp(fn, stream, seconds):
+    """Untimed launches back to back for `seconds` of wall time before the
+    warmup and the timed steps: the GPU clock leaves its idle state over the
+    first tens of milliseconds of load, and a fixed time (not a launch count)
+    covers that for any workload size."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        stream.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "launches": n}
 
 
 def timing_trials(fn, stream, trials=20, per=10):
@@ -233,6 +250,7 @@ def main():
     fwd = fa.flash_attn_fwd if w.dtype == "bf16" else fa.flash_attn_fwd_f32
 
     stream = torch.cuda.current_stream()
+    ramp = clock_ramp(lambda: fwd(q, k, v, o, lse, w.scale, causal), stream, args.ramp_seconds)
     for _ in range(args.warmup):
         fwd(q, k, v, o, lse, w.scale, causal)
     torch.cuda.synchronize()
@@ -289,6 +307,7 @@ def main():
         },
         "roofline": roofline,
         "wall_s_timed_region": round(wall_s, 4),
+        "clock_ramp": ramp,
     }
     step = lambda: fwd(q, k, v, o, lse, w.scale, causal)  # noqa: E731
     result["timing"] = timing_trials(step, stream)
@@ -391,6 +410,7 @@ def bench_kv(args, w):
             fa.flash_attn_fwd_kv(q, k, v, o, lse, w.scale, w.causal, splits, ws)
 
     stream = torch.cuda.current_stream()
+    ramp = clock_ramp(step, stream, args.ramp_seconds)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -433,6 +453,7 @@ def bench_kv(args, w):
                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                       "traffic": None}),
         "wall_s_timed_region": round(wall_s, 4),
+        "clock_ramp": ramp,
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -188,17 +188,18 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *     returned them for the same q, k, v, scale, causal).
  *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]: outputs (bf16 bits); with GQA dk and dv
  *     of a K/V head sum over its Hq/Hkv query heads.
- *   workspace: caller-owned device buffer of at least
- *     flash_attn_bwd_workspace_bytes(B,Hq,Hkv,N,d) bytes; its contents on entry
- *     are ignored and on return are unspecified.
+ *   workspace, workspace_bytes: caller-owned device buffer and its size in
+ *     bytes, at least flash_attn_bwd_workspace_bytes(B,Hq,Hkv,N,d); its
+ *     contents on entry are ignored and on return are unspecified. A NULL or
+ *     shorter workspace gives FA_ERR_WORKSPACE before any device work.
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
 
 /* Backward, fp32 check mode: as flash_attn_bwd with fp32 tensors. */
 int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
-                       const float* dout, float* dq, float* dk, float* dv, void* workspace,
+                       const float* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
 
 /* Static, NUL-terminated name of a status code ("FA_OK", ...); "FA_UNKNOWN" otherwise. */

@@ -65,9 +65,9 @@ def load_library():
     lib.flash_attn_fwd.restype = I
     lib.flash_attn_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.flash_attn_fwd_f32.restype = I
-    lib.flash_attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P]
+    lib.flash_attn_bwd.argtypes = [P] * 10 + [Z, I, I, I, I, I, F, I, P]
     lib.flash_attn_bwd.restype = I
-    lib.flash_attn_bwd_f32.argtypes = [P] * 10 + [I, I, I, I, I, F, I, P]
+    lib.flash_attn_bwd_f32.argtypes = [P] * 10 + [Z, I, I, I, I, I, F, I, P]
     lib.flash_attn_bwd_f32.restype = I
     lib.flash_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.flash_attn_bwd_workspace_bytes.restype = Z
@@ -118,18 +118,50 @@ def _check(*tensors, dtype=None):
             raise ValueError(f"expected dtype {dtype}, got {t.dtype}")
 
 
+def _expect_shape(what, t, shape):
+    """The C ABI sees only pointers: a tensor of another shape would be read or
+    written out of bounds on the GPU, so every shape is checked here first."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor")
+    if tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _dims(q, k):
+    import torch
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise TypeError("expected torch tensors")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
-    B, Hq, N, d = q.shape
-    return int(B), int(Hq), int(k.shape[1]), int(N), int(d)
+    B, Hq, N, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[1])
+    _expect_shape("k", k, (B, Hkv, N, d))
+    return B, Hq, Hkv, N, d
+
+
+def _check_fwd_shapes(q, k, v, o, lse):
+    B, Hq, Hkv, N, d = _dims(q, k)
+    _expect_shape("v", v, (B, Hkv, N, d))
+    _expect_shape("o", o, (B, Hq, N, d))
+    _expect_shape("lse", lse, (B, Hq, N))
+    return B, Hq, Hkv, N, d
+
+
+def _check_bwd_shapes(q, k, v, o, lse, dout, dq, dk, dv):
+    B, Hq, Hkv, N, d = _check_fwd_shapes(q, k, v, o, lse)
+    for what, t in (("dout", dout), ("dq", dq)):
+        _expect_shape(what, t, (B, Hq, N, d))
+    for what, t in (("dk", dk), ("dv", dv)):
+        _expect_shape(what, t, (B, Hkv, N, d))
+    return B, Hq, Hkv, N, d
 
 
 def _fwd(name, dt, q, k, v, o, lse, scale, causal, stream):
     import torch
+    B, Hq, Hkv, N, d = _check_fwd_shapes(q, k, v, o, lse)
     _check(q, k, v, o, dtype=dt)
     _check(lse, dtype=torch.float32)
-    B, Hq, Hkv, N, d = _dims(q, k)
     st = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream(stream))
     if st != 0:
@@ -154,15 +186,15 @@ def flash_attn_bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
 
 def _bwd(name, dt, q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal, stream):
     import torch
+    B, Hq, Hkv, N, d = _check_bwd_shapes(q, k, v, o, lse, dout, dq, dk, dv)
     _check(q, k, v, o, dout, dq, dk, dv, dtype=dt)
     _check(lse, dtype=torch.float32)
     _check(workspace)
-    B, Hq, Hkv, N, d = _dims(q, k)
     need = flash_attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)
-    if workspace.numel() * workspace.element_size() < need:
+    if _ws_size(workspace) < need:
         raise ValueError(f"workspace too small: need {need} bytes")
     st = getattr(load_library(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _ws_size(workspace),
                                        B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream(stream))
     if st != 0:
         raise FlashAttnError(name, st)
@@ -219,18 +251,50 @@ def _ws_size(workspace):
     return 0 if workspace is None else workspace.numel() * workspace.element_size()
 
 
-def flash_attn_fwd_kv(q, k, v, o, lse, scale, causal, num_splits=1, workspace=None, stream=None):
-    """bf16 forward with Nq queries and Nk keys (bottom-right causal), optionally
-    split over keys: q, o [B,Hq,Nq,d], k, v [B,Hkv,Nk,d], lse [B,Hq,Nq] fp32."""
+def _check_kv_shapes(q, k, v, o, lse):
     import torch
-    _check(q, k, v, o, dtype=torch.bfloat16)
-    _check(lse, dtype=torch.float32)
-    if workspace is not None:
-        _check(workspace)
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise TypeError("expected torch tensors")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
     B, Hq, Nq, d = (int(x) for x in q.shape)
     Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    _expect_shape("k", k, (B, Hkv, Nk, d))
+    _expect_shape("v", v, (B, Hkv, Nk, d))
+    _expect_shape("o", o, (B, Hq, Nq, d))
+    _expect_shape("lse", lse, (B, Hq, Nq))
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _check_varlen_shapes(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k):
+    import torch
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise TypeError("expected torch tensors")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [Hq, Tq, d] and k, v [Hkv, Tk, d]")
+    Hq, Tq, d = (int(x) for x in q.shape)
+    Hkv, Tk = int(k.shape[0]), int(k.shape[1])
+    _expect_shape("k", k, (Hkv, Tk, d))
+    _expect_shape("v", v, (Hkv, Tk, d))
+    _expect_shape("o", o, (Hq, Tq, d))
+    _expect_shape("lse", lse, (Hq, Tq))
+    for what, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 1 or t.numel() < 2:
+            raise ValueError(f"{what} must be a 1-D tensor of B+1 >= 2 offsets")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError(f"cu_seqlens_k has {cu_seqlens_k.numel()} entries, cu_seqlens_q {cu_seqlens_q.numel()}")
+    return int(cu_seqlens_q.numel()) - 1, Hq, Hkv, Tq, Tk, d
+
+
+def flash_attn_fwd_kv(q, k, v, o, lse, scale, causal, num_splits=1, workspace=None, stream=None):
+    """bf16 forward with Nq queries and Nk keys (bottom-right causal), optionally
+    split over keys: q, o [B,Hq,Nq,d], k, v [B,Hkv,Nk,d], lse [B,Hq,Nq] fp32."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _check_kv_shapes(q, k, v, o, lse)
+    _check(q, k, v, o, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    if workspace is not None:
+        _check(workspace)
     st = load_library().flash_attn_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                                           float(scale), int(bool(causal)), int(num_splits), _ptr(workspace),
                                           _ws_size(workspace), _stream(stream))
@@ -243,16 +307,12 @@ def flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     """bf16 forward over a variable-length batch: q, o [Hq,Tq,d], k, v [Hkv,Tk,d],
     lse [Hq,Tq] fp32, cu_seqlens_* int32 [B+1] on the GPU."""
     import torch
+    B, Hq, Hkv, Tq, Tk, d = _check_varlen_shapes(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k)
     _check(q, k, v, o, dtype=torch.bfloat16)
     _check(lse, dtype=torch.float32)
     _check(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
     if workspace is not None:
         _check(workspace)
-    if q.dim() != 3 or k.dim() != 3:
-        raise ValueError("q must be [Hq, Tq, d] and k, v [Hkv, Tk, d]")
-    Hq, Tq, d = (int(x) for x in q.shape)
-    Hkv, Tk = int(k.shape[0]), int(k.shape[1])
-    B = int(cu_seqlens_q.numel()) - 1
     st = load_library().flash_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
                                               _ptr(cu_seqlens_k), B, Hq, Hkv, Tq, Tk, int(max_seqlen_q),
                                               int(max_seqlen_k), d, float(scale), int(bool(causal)),
@@ -306,10 +366,10 @@ def flash_attn_naive_fwd(q, k, v, o, lse, scale, causal, workspace, stream=None)
     """Three-pass materialising baseline (bf16): same arguments as flash_attn_fwd
     plus a workspace of flash_attn_naive_workspace_bytes(B, Hq, N) bytes."""
     import torch
+    B, Hq, Hkv, N, d = _check_fwd_shapes(q, k, v, o, lse)
     _check(q, k, v, o, dtype=torch.bfloat16)
     _check(lse, dtype=torch.float32)
     _check(workspace)
-    B, Hq, Hkv, N, d = _dims(q, k)
     st = load_library().flash_attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                                              float(scale), int(bool(causal)), _ptr(workspace), _ws_size(workspace),
                                              _stream(stream))

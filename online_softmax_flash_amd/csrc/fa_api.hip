@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "flash_attn.h"
 #include "fa_launch.hpp"
 
@@ -56,7 +57,7 @@ int fwd_common(bool f32, const void* q, const void* k, const void* v, void* o, f
 }
 
 int bwd_common(bool f32, const void* q, const void* k, const void* v, const void* o, const float* lse,
-               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   int st = check_ptrs(ptrs, 9);
@@ -65,6 +66,7 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
   if (st != FA_OK) return st;
   if (workspace == nullptr) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if (workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)) return FA_ERR_WORKSPACE;
   const float c = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* dsum = static_cast<float*>(workspace);
@@ -177,17 +179,17 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 }
 
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
-  return bwd_common(false, q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
-                    stream);
+  return bwd_common(false, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d, scale,
+                    causal, stream);
 }
 
 int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
-                       const float* dout, float* dq, float* dk, float* dv, void* workspace,
+                       const float* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
-  return bwd_common(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
-                    stream);
+  return bwd_common(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d, scale,
+                    causal, stream);
 }
 
 int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {

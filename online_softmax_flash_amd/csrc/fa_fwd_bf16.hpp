@@ -36,6 +36,7 @@
 //    most for short sequences, with few blocks per item).
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -542,17 +543,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device. The cache entries
+// are atomics: concurrent first calls from several host threads each store
+// the same value, so the library stays safe to call from any thread.
 inline int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D, int BN, int NW, bool CAUSAL>

@@ -34,10 +34,9 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 def assert_close(got, ref, dtype, what, lse=False, ref_scale=None):
     """Compare against the oracle. fp32 mode is normwise: max|diff| over
-    max|ref|, where ``ref_scale`` (default max|ref|) may name the magnitude of
-    a whole family of outputs -- dQ, dK and dV together -- so that an output
-    that is exactly zero in exact arithmetic (dQ and dK when N = 1) is judged
-    against the size of the terms that cancel in it."""
+    max|ref| of this output. ``ref_scale`` replaces max|ref| only for an
+    output that is exactly zero in exact arithmetic (dQ and dK when N = 1),
+    which is then judged against the size of the terms that cancel in it."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"

@@ -58,10 +58,10 @@ def _fwd(fn="flash_attn_fwd", ptrs=(FAKE,) * 5, shape=OK_SHAPE, scale=0.1, causa
     return getattr(lib, fn)(*p, *shape, ctypes.c_float(scale), causal, None)
 
 
-def _bwd(fn="flash_attn_bwd", ptrs=(FAKE,) * 10, shape=OK_SHAPE, scale=0.1, causal=0):
+def _bwd(fn="flash_attn_bwd", ptrs=(FAKE,) * 10, shape=OK_SHAPE, scale=0.1, causal=0, ws_bytes=1 << 40):
     lib = fa.load_library()
     p = [ctypes.c_void_p(x) if x else None for x in ptrs]
-    return getattr(lib, fn)(*p, *shape, ctypes.c_float(scale), causal, None)
+    return getattr(lib, fn)(*p, ctypes.c_size_t(ws_bytes), *shape, ctypes.c_float(scale), causal, None)
 
 
 @pytest.mark.parametrize("fn", ["flash_attn_fwd", "flash_attn_fwd_f32"])
@@ -95,6 +95,11 @@ def test_backward_validation(fn):
     assert _bwd(fn, ptrs) == STATUS["FA_ERR_WORKSPACE"]
     ptrs[9] = FAKE + 2
     assert _bwd(fn, ptrs) == STATUS["FA_ERR_ALIGN"]
+    # A workspace shorter than flash_attn_bwd_workspace_bytes is refused before any device work.
+    need = fa.flash_attn_bwd_workspace_bytes(*OK_SHAPE)
+    assert need > 0
+    assert _bwd(fn, ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
+    assert _bwd(fn, ws_bytes=0) == STATUS["FA_ERR_WORKSPACE"]
     assert _bwd(fn, shape=(2, 8, 3, 100, 128)) == STATUS["FA_ERR_SHAPE"]
     assert _bwd(fn, shape=(2, 8, 2, 100, 48)) == STATUS["FA_ERR_UNSUPPORTED"]
     assert _bwd(fn, scale=math.nan) == STATUS["FA_ERR_SCALE"]
@@ -186,3 +191,4 @@ def test_naive_rejects_bad_arguments_and_sizes_workspace():
     # quadratic in N: N*N fp32 scores plus N*N bf16 weights per head
     assert fa.flash_attn_naive_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 4096 * 6
     assert fa.flash_attn_naive_workspace_bytes(0, 16, 4096) == 0
+

@@ -54,10 +54,14 @@ def test_bwd_small_full_parity(shape, causal, dtype):
     scale = 1.0 / math.sqrt(d)
     dq, dk, dv = run_fwd_bwd(inp, scale, causal)
     rq, rk, rv = oracle.attn_bwd_analytic(inp.q, inp.k, inp.v, inp.do, scale, causal)
-    fam = max(float(np.abs(x).max()) for x in (rq, rk, rv))
+    # fp32 check mode: each gradient against its own max|ref| (normwise 1e-5).
+    # Only at N = 1 are dQ and dK exactly zero in exact arithmetic (one key:
+    # dS = P (dP - D) = 0); there the size of the cancelling terms, taken as
+    # the largest of the three gradients, is the normaliser.
+    fam = max(float(np.abs(x).max()) for x in (rq, rk, rv)) if N == 1 else None
     assert_close(from_dev(dq), rq, dtype, f"dQ {shape} causal={causal}", ref_scale=fam)
     assert_close(from_dev(dk), rk, dtype, f"dK {shape} causal={causal}", ref_scale=fam)
-    assert_close(from_dev(dv), rv, dtype, f"dV {shape} causal={causal}", ref_scale=fam)
+    assert_close(from_dev(dv), rv, dtype, f"dV {shape} causal={causal}")
 
 
 FULL = [("bwd_4k", True, 3), ("gqa_4k", True, 1), ("wide_4k", False, 1)]

@@ -118,6 +118,49 @@ def test_fwd_full_size_sampled(name, causal):
     print(f"{name} causal={causal}: worst sampled max-abs {worst:.3e}")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_fwd_2k_every_element(causal):
+    """The B=4, H=32, N=2048, d=128 workload (seed 1) compared on every
+    element of O and lse: 1024 work items on one persistent workgroup per
+    compute unit, so every workgroup runs several items (the mirrored item
+    order of odd rounds, the next item's first K/V block copied into the
+    stage the last block freed, its query rows read behind the last block's
+    score products)."""
+    w = WORKLOADS["fwd_2k"]
+    announce(f"fwd every element fwd_2k causal={causal} seed={w.seed}")
+    inp = make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, seed=w.seed, dtype=w.dtype)
+    o, lse = run_fwd(inp, w.scale, causal)
+    O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, inp.k, inp.v, w.scale, causal)
+    assert_close(from_dev(o), O_ref, "bf16", f"fwd_2k O causal={causal}")
+    assert_close(from_dev(lse), L_ref, "bf16", f"fwd_2k lse causal={causal}", lse=True)
+
+
+MULTI_ROUND = [
+    # B, Hq, Hkv, N, d: 4 query blocks of 256 x 128 heads = 512 items, two
+    # rounds over 256 persistent workgroups; ragged N; GQA and MQA-like groups.
+    (2, 64, 64, 1000, 64),
+    (2, 64, 16, 1000, 128),
+    (2, 64, 64, 1024, 128),
+    (1, 128, 8, 777, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", MULTI_ROUND, ids=["x".join(map(str, s)) for s in MULTI_ROUND])
+def test_fwd_multi_round_every_element(shape, causal):
+    """More work items than compute units at d <= 128: each persistent
+    workgroup runs a second item (and the hand-off between items), compared
+    element by element against the oracle."""
+    B, Hq, Hkv, N, d = shape
+    announce(f"fwd multi-round shape={shape} causal={causal} seed=13")
+    inp = make_inputs(B, Hq, Hkv, N, d, seed=13)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_fwd(inp, scale, causal)
+    O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, inp.k, inp.v, scale, causal)
+    assert_close(from_dev(o), O_ref, "bf16", f"O {shape} causal={causal}")
+    assert_close(from_dev(lse), L_ref, "bf16", f"lse {shape} causal={causal}", lse=True)
+
+
 def test_fwd_repeatable_and_allocation_free():
     """Two runs give identical bits; a call allocates no device memory."""
     w = WORKLOADS["fwd_2k"]
