@@ -76,7 +76,8 @@ typedef enum {
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   FA_ERR_SCALE = 5,       /* scale is not finite or is negative */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  FA_ERR_WORKSPACE = 7    /* a required workspace is NULL or smaller than its *_workspace_bytes */
+  FA_ERR_WORKSPACE = 7,   /* a required workspace is NULL or smaller than its *_workspace_bytes */
+  FA_ERR_SCRATCH = 8      /* flash_attn_fwd_kv_noalloc: the split partials exceed FLASH_ATTN_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -142,6 +143,32 @@ int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
                           const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
                           int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
                           int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flash_attn_fwd_kv without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it. Same
+ * arguments, result and errors as flash_attn_fwd_kv (the caller still passes
+ * q, k, v, o and lse); the split partials go to a static device array of
+ * FLASH_ATTN_SCRATCH_BYTES inside the library, one per device, held until the
+ * process ends.
+ *   num_splits: as flash_attn_fwd_kv, except that 0 takes the library's count
+ *     lowered until the partials (flash_attn_fwd_kv_workspace_bytes) fit the
+ *     scratch; an explicit count whose partials do not fit gives
+ *     FA_ERR_SCRATCH before any device work.
+ * Every call on one device shares that device's scratch and leaves its own
+ * partials there: calls that overlap in time on one device (two streams, two
+ * host threads) race and must be ordered by the caller. Nothing in the
+ * scratch needs to start at zero. The first call on a device is its set-up:
+ * it looks up the scratch's address on that device (hipGetSymbolAddress;
+ * FA_ERR_HIP if that fails), which makes the HIP runtime map the scratch onto
+ * the device once; make that first call before capturing a graph or entering
+ * a loop that must not see device memory change. Later calls allocate nothing.
+ */
+#define FLASH_ATTN_SCRATCH_BYTES (32u << 20)
+int flash_attn_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                              int num_splits, void* stream);
 
 /* Split count the library picks for num_splits = 0 (Nq, Nk: the largest
  * sequence lengths); 0 for invalid sizes. */

@@ -25,6 +25,7 @@ __all__ = [
     "flash_attn_status_str",
     "flash_attn_fwd_kv",
     "flash_attn_fwd_varlen",
+    "flash_attn_fwd_kv_noalloc",
     "flash_attn_fwd_kv_num_splits",
     "flash_attn_fwd_kv_workspace_bytes",
     "attention_forward",
@@ -74,6 +75,8 @@ def load_library():
     L = ctypes.c_longlong
     lib.flash_attn_fwd_kv.argtypes = [P] * 5 + [I] * 6 + [F, I, I, P, Z, P]
     lib.flash_attn_fwd_kv.restype = I
+    lib.flash_attn_fwd_kv_noalloc.argtypes = [P] * 5 + [I] * 6 + [F, I, I, P]
+    lib.flash_attn_fwd_kv_noalloc.restype = I
     lib.flash_attn_fwd_varlen.argtypes = [P] * 7 + [I] * 8 + [F, I, I, P, Z, P]
     lib.flash_attn_fwd_varlen.restype = I
     lib.flash_attn_fwd_kv_num_splits.argtypes = [I] * 6
@@ -300,6 +303,20 @@ def flash_attn_fwd_kv(q, k, v, o, lse, scale, causal, num_splits=1, workspace=No
                                           _ws_size(workspace), _stream(stream))
     if st != 0:
         raise FlashAttnError("flash_attn_fwd_kv", st)
+
+
+def flash_attn_fwd_kv_noalloc(q, k, v, o, lse, scale, causal, num_splits=0, stream=None):
+    """flash_attn_fwd_kv with the split partials in the library's static
+    scratch: no workspace, no device allocation (FLASH_ATTN_SCRATCH_BYTES)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _check_kv_shapes(q, k, v, o, lse)
+    _check(q, k, v, o, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    st = load_library().flash_attn_fwd_kv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                                                  Nk, d, float(scale), int(bool(causal)), int(num_splits),
+                                                  _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_fwd_kv_noalloc", st)
 
 
 def flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal,

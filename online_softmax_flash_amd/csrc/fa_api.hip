@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 
 #include "flash_attn.h"
 #include "fa_launch.hpp"
@@ -101,9 +102,36 @@ size_t kv_workspace(long long rows, int d, int splits) {
   return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
 }
 
+// Static scratch of flash_attn_fwd_kv_noalloc: the split partials live in
+// this file-scope device array instead of a caller's workspace. Each device
+// the library runs on holds its own copy until the process ends. In host code
+// `scratch` is only a stand-in for the symbol, never a device address: the
+// address is taken once per device with hipGetSymbolAddress (with that device
+// current) and kept in g_scratch_ptr, and only that pointer reaches kernels.
+static __device__ __align__(256) uint8_t scratch[FLASH_ATTN_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device; concurrent first calls store the same address).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FA_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FA_OK;
+}
+
+// use_scratch: the split partials go to the static scratch (no workspace
+// argument); num_splits = 0 then picks the library's count capped so that the
+// partials fit, and an explicit count whose partials do not fit is refused.
 int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q, const int* cu_k,
               int B, int Hq, int Hkv, int Nq, int Nk, int max_nq, int max_nk, int d, float scale, int causal,
-              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+              int num_splits, void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
   const void* ptrs[] = {q, k, v, o, lse};
   int st = check_ptrs(ptrs, 5);
   if (st != FA_OK) return st;
@@ -120,8 +148,18 @@ int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, 
   if ((long long)max_nq * G > 0x7fffffffLL || nrb * 256 > 0x7fffffffLL || Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  const int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk) : num_splits;
+  int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk) : num_splits;
   if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
+  if (use_scratch && splits > 1) {
+    if (num_splits == 0)
+      while (splits > 1 && kv_workspace(rows, d, splits) > (size_t)FLASH_ATTN_SCRATCH_BYTES) --splits;
+    if (kv_workspace(rows, d, splits) > (size_t)FLASH_ATTN_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    if (splits > 1) {
+      st = scratch_ptr(&workspace);
+      if (st != FA_OK) return st;
+      workspace_bytes = FLASH_ATTN_SCRATCH_BYTES;
+    }
+  }
   if (splits > 1) {
     if (workspace == nullptr) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -210,6 +248,13 @@ int flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, floa
                    workspace, workspace_bytes, stream);
 }
 
+int flash_attn_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                              int num_splits, void* stream) {
+  return kv_common(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, Nq, Nk, d, scale, causal, num_splits,
+                   nullptr, 0, stream, true);
+}
+
 int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                           const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
                           int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
@@ -255,6 +300,7 @@ const char* flash_attn_status_str(int status) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE";
     case FA_ERR_HIP: return "FA_ERR_HIP";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH";
     default: return "FA_UNKNOWN";
   }
 }

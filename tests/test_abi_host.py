@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libfl
 FAKE = 0x10000  # non-null, 16-byte aligned; never dereferenced (validation fails first)
 OK_SHAPE = (2, 8, 2, 100, 128)
 STATUS = {"FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3, "FA_ERR_ALIGN": 4,
-          "FA_ERR_SCALE": 5, "FA_ERR_HIP": 6, "FA_ERR_WORKSPACE": 7}
+          "FA_ERR_SCALE": 5, "FA_ERR_HIP": 6, "FA_ERR_WORKSPACE": 7, "FA_ERR_SCRATCH": 8}
 
 
 def declared_functions():
@@ -192,3 +192,23 @@ def test_naive_rejects_bad_arguments_and_sizes_workspace():
     assert fa.flash_attn_naive_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 4096 * 6
     assert fa.flash_attn_naive_workspace_bytes(0, 16, 4096) == 0
 
+
+def test_noalloc_refuses_partials_beyond_its_scratch():
+    """flash_attn_fwd_kv_noalloc checks its arguments like flash_attn_fwd_kv and
+    refuses, before any device work, an explicit split count whose partials
+    exceed the static scratch (FLASH_ATTN_SCRATCH_BYTES = 32 MiB)."""
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(FAKE)] * 5
+
+    def call(shape, splits, ptrs=p, causal=1):
+        return lib.flash_attn_fwd_kv_noalloc(*ptrs, *shape, ctypes.c_float(0.1), causal, splits, None)
+
+    big = (64, 64, 8, 64, 4096, 256)  # 262144 rows x 256 fp32 per split
+    assert fa.flash_attn_fwd_kv_workspace_bytes(64 * 64 * 64, 256, 8) > 32 << 20
+    assert call(big, 8) == STATUS["FA_ERR_SCRATCH"]
+    assert call((2, 8, 2, 3, 100, 128), 1, ptrs=[ctypes.c_void_p(FAKE)] * 4 + [None]) == STATUS["FA_ERR_NULL"]
+    assert call((2, 8, 3, 3, 100, 128), 2) == STATUS["FA_ERR_SHAPE"]
+    assert call((2, 8, 2, 3, 100, 96), 2) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert call((2, 8, 2, 3, 100, 128), 300) == STATUS["FA_ERR_SHAPE"]
+    src = open(HEADER).read()
+    assert re.search(r"#define FLASH_ATTN_SCRATCH_BYTES \(32u << 20\)", src)
