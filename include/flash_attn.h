@@ -200,16 +200,22 @@ size_t flash_attn_naive_workspace_bytes(int B, int Hq, int N);
 
 /*
  * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these
- * sizes: two fp32 per query row (D_i = sum_c dO_ic O_ic, and lse_i * log2(e)),
- * 4*(R64 + R) bytes with R = B*Hq*N and R64 = R rounded up to a multiple of
- * 64, rounded up to 256. Linear in N: no N x N buffer. Returns 0 for invalid
- * sizes.
+ * sizes: per query row two fp32 (D_i = sum_c dO_ic O_ic, and lse_i * log2(e))
+ * and d fp32 (the accumulator the bf16 backward sums dQ in, over key blocks):
+ * 2*A(4R) + A(4*R*d) bytes with R = B*Hq*N and A() rounding up to a multiple
+ * of 256. Linear in N: no N x N buffer. Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /*
  * Backward, bf16 storage, fp32 accumulation. Recomputes every score block from
- * q, k and the forward's lse; returns the gradients of sum(dout * O).
+ * q, k and the forward's lse; returns the gradients of sum(dout * O). For
+ * d <= 128 every score block is recomputed once and gives dK, dV and its
+ * share of dQ (five products per pair of blocks); the shares of dQ are added
+ * into the workspace's fp32 accumulator with atomic adds, in an order that
+ * varies from run to run, so dq may differ in its last bits between runs
+ * (dk and dv do not). At d = 256 dQ comes from a second kernel that
+ * recomputes the scores (seven products) and all outputs are repeatable.
  *   q, o, dout [B,Hq,N,d], k, v [B,Hkv,N,d] (bf16 bits), lse [B,Hq,N] fp32:
  *     the forward's inputs and outputs (o and lse exactly as flash_attn_fwd
  *     returned them for the same q, k, v, scale, causal).

@@ -71,9 +71,37 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
   const float c = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* dsum = static_cast<float*>(workspace);
-  const hipError_t e =
-      f32 ? fa::bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s)
-          : fa::bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
+  hipError_t e;
+  if (f32) {
+    e = fa::bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
+  } else if (d <= 128) {
+    // One pass over the score blocks (dK, dV and dQ together).
+    fa::BwdKvArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    const long long rows = (long long)B * Hq * N;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.dsum = dsum;
+    a.l2 = reinterpret_cast<float*>(ws + fa::bwd_ws_l2_offset(rows));
+    a.dqa = reinterpret_cast<float*>(ws + fa::bwd_ws_dqa_offset(rows));
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Nq = a.Nk = a.max_nq = a.max_nk = N;
+    a.rows = rows;
+    a.c = c;
+    a.scale = scale;
+    e = fa::bwd_fused_bf16(a, d, causal, s);
+  } else {
+    e = fa::bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -209,11 +237,9 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shape(B, Hq, Hkv, N, d, 0) != FA_OK) return 0;
-  // D (fp32 per query row), then lse * log2(e) (fp32 per query row) from the
-  // next 256-byte boundary.
-  const size_t rows = (size_t)B * Hq * N;
-  const size_t bytes = 4 * (((rows + 63) / 64) * 64 + rows);
-  return (bytes + 255) & ~(size_t)255;
+  // D (fp32 per query row), lse * log2(e) (fp32 per query row) and the fp32
+  // dQ accumulator (d per query row), each from a 256-byte boundary.
+  return fa::bwd_ws_bytes((long long)B * Hq * N, d);
 }
 
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -28,6 +28,7 @@
 
 #include "fa_bwd.hpp"
 #include "fa_fwd_bf16.hpp"
+#include "fa_launch.hpp"
 
 namespace fa {
 
@@ -67,11 +68,31 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdArgs a, float* l2
 
 // Direct copy of 64 per-row fp32 values (rows r0 .. r0+63 of one head, taken
 // in rho order within each 32) into 256 bytes of LDS: lane l writes bytes
-// 4l .. 4l+3. Rows >= N read row N-1 (the caller masks them).
+// 4l .. 4l+3. Rows >= N read row N-1 (the caller masks them). Issued through
+// inline assembly like dma16 (the compiler does not track it, so it inserts
+// no wait for it before later LDS accesses or fences): callers wait (vmcnt)
+// and synchronise before the destination is read.
 __device__ __forceinline__ void dma_row_stats(uint8_t* lds, const float* g, int r0, int N, int lane) {
   int r = r0 + 32 * (lane >> 5) + rho(lane & 31);
   r = r < N ? r : N - 1;
-  __builtin_amdgcn_global_load_lds(g + r, (lds_void_t*)lds, 4, 0, 0);
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
+  const uint64_t gs = uniform_u64((uint64_t)g);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0v), "v"((uint32_t)r * 4u), "s"(gs)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Workgroup barrier that orders LDS accesses only: waits for this wave's own
+// LDS operations (lgkmcnt), not for its global loads, direct-to-LDS copies or
+// atomics in flight, which a plain __syncthreads() would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Transposing read of a 16-bit fragment: two ds_read_b64_tr_b16, ROWB2 bytes apart.
@@ -232,7 +253,7 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
         pack_frag(bfr[sub][1], p + 8);
       }
     }
-    __syncthreads();  // barrier 2: P visible to the dS waves
+    lds_barrier();  // barrier 2: P visible to the dS waves (the next step's copies stay in flight)
     if (!pwave) {
       // dS = P (dP - D) in bf16 fragments.
 #pragma unroll
@@ -401,9 +422,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
   }
 }
 
-// Workspace layout of the bf16 backward: D [B*Hq*N] fp32, then l2 [B*Hq*N]
-// fp32 starting at the next 256-byte boundary.
-inline size_t bwd_l2_offset_floats(long long rows) { return (size_t)((rows + 63) / 64) * 64; }
 
 // The dQ kernel's instances live in their own translation unit (built with
 // MFMA accumulators in VGPRs, which keeps it within two waves per SIMD).
@@ -415,7 +433,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   // it; at d = 256 a wave needs more than half the register file, so 2.
   constexpr int NPKV = D <= 128 ? 4 : 2;
   const long long rows = (long long)a.B * a.Hq * a.N;
-  float* l2 = a.dsum + bwd_l2_offset_floats(rows);
+  float* l2 = a.dsum + bwd_ws_l2_offset(rows) / 4;  // the workspace layout of bwd_ws_bytes
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a,
                      l2);

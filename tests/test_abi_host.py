@@ -107,10 +107,14 @@ def test_backward_validation(fn):
 
 def test_workspace_bytes_linear_in_n():
     ws = fa.flash_attn_bwd_workspace_bytes
-    # two fp32 per query row: D, then lse * log2(e) from a 64-row boundary
-    assert ws(2, 16, 16, 4096, 128) == 8 * 2 * 16 * 4096
-    assert ws(1, 1, 1, 1, 64) == 512
-    assert ws(1, 2, 1, 1000, 64) == ((4 * (2048 + 2000) + 255) // 256) * 256
+    # Per query row: D and lse * log2(e) (fp32 each), then the fp32 dQ
+    # accumulator (d values), each part from a 256-byte boundary.
+    def up(n):
+        return (n + 255) // 256 * 256
+    R = 2 * 16 * 4096
+    assert ws(2, 16, 16, 4096, 128) == 2 * 4 * R + 4 * R * 128
+    assert ws(1, 1, 1, 1, 64) == 2 * 256 + 256
+    assert ws(1, 2, 1, 1000, 64) == 2 * up(4 * 2000) + up(4 * 2000 * 64)
     assert ws(2, 16, 16, 8192, 128) == 2 * ws(2, 16, 16, 4096, 128)
     assert ws(0, 1, 1, 1, 64) == 0
     assert ws(1, 3, 2, 1, 64) == 0
