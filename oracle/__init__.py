@@ -30,5 +30,6 @@ from .attention import (  # noqa: F401
     kv_head,
     merge_partials,
     attn_fwd_varlen,
+    attn_bwd_varlen,
 )
 from .online_fold import attn_fwd_online_fold, fold_head  # noqa: F401

@@ -37,7 +37,9 @@ and k, v [Hkv, Tk, d], sequence b owning query rows cu_q[b] .. cu_q[b+1]-1 and
 key rows cu_k[b] .. cu_k[b+1]-1; each sequence is an independent problem.
 
 The backward is derived from that definition by the chain rule (the pages only
-say the score blocks are recomputed from the saved statistics):
+say the score blocks are recomputed from the saved statistics), for the same
+problems as the forward (square, rectangular with the bottom-right mask,
+variable-length batches):
 ``dV = P^T dO``, ``dP = dO V^T``, ``D_i = sum_j P_ij dP_ij``,
 ``dS = P * (dP - D)``, ``dQ = scale dS K``, ``dK = scale dS^T Q``. With grouped
 K/V heads (GQA) query head hq reads K/V head ``hq // (Hq / Hkv)`` and dK, dV of
@@ -57,6 +59,7 @@ __all__ = [
     "attn_bwd_analytic",
     "merge_partials",
     "attn_fwd_varlen",
+    "attn_bwd_varlen",
 ]
 
 
@@ -139,19 +142,23 @@ def attn_fwd_materialised(q, k, v, scale, causal, rows=None):
 def attn_bwd_group(q_g, k_h, v_h, do_g, scale, causal):
     """Backward of one K/V head and the G query heads that read it.
 
-    q_g, do_g: [G, N, d]; k_h, v_h: [N, d]. Returns dq [G, N, d], dk [N, d],
-    dv [N, d] (float64), the gradients of sum(dO * O).
+    q_g, do_g: [G, Nq, d]; k_h, v_h: [Nk, d]. Returns dq [G, Nq, d], dk [Nk, d],
+    dv [Nk, d] (float64), the gradients of sum(dO * O). With Nq != Nk the
+    causal mask is the forward's, aligned to the bottom right (query i sees
+    key j iff j <= i + Nk - Nq). A query row that sees no key has O = 0 for
+    any q, k, v: its dq is 0 and it adds nothing to dk and dv (its P row is
+    0, so is its dS row).
     """
     q_g = np.asarray(q_g, dtype=np.float64)
     do_g = np.asarray(do_g, dtype=np.float64)
     k_h = np.asarray(k_h, dtype=np.float64)
     v_h = np.asarray(v_h, dtype=np.float64)
-    G, N, _ = q_g.shape
+    G, Nq, _ = q_g.shape
+    Nk = k_h.shape[0]
     dq = np.empty_like(q_g)
     dk = np.zeros_like(k_h)
     dv = np.zeros_like(v_h)
-    r = np.arange(N)
-    vis = _visible(r, k_h.shape[0], causal)
+    vis = _visible(np.arange(Nq), Nk, causal, Nk - Nq)
     for j in range(G):
         S = np.where(vis, _scores(q_g[j], k_h, scale), -np.inf)
         P, _, _ = _softmax_rows(S)
@@ -165,8 +172,9 @@ def attn_bwd_group(q_g, k_h, v_h, do_g, scale, causal):
 
 
 def attn_bwd_analytic(q, k, v, do, scale, causal):
-    """Backward over all heads: returns dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] (float64)."""
-    B, Hq, N, d = q.shape
+    """Backward over all heads: q, do [B,Hq,Nq,d], k, v [B,Hkv,Nk,d]; returns
+    dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] (float64)."""
+    B, Hq, Nq, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     if Hq % Hkv:
@@ -230,3 +238,30 @@ def attn_fwd_varlen(q, k, v, cu_q, cu_k, scale, causal):
                 continue  # no keys: O = 0, lse = -inf
             O[hq, q0:q1], lse[hq, q0:q1] = attn_fwd_head(q[hq, q0:q1], k[g, k0:k1], v[g, k0:k1], scale, causal)
     return O, lse
+
+
+def attn_bwd_varlen(q, k, v, do, cu_q, cu_k, scale, causal):
+    """Backward of a variable-length batch (the packing of attn_fwd_varlen):
+    q, do [Hq, Tq, d], k, v [Hkv, Tk, d]; sequence b owns query rows
+    cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1], each sequence an
+    independent problem (bottom-right causal mask when its lengths differ).
+    Returns dq [Hq, Tq, d], dk, dv [Hkv, Tk, d] (float64); rows outside every
+    sequence, and every row of a sequence without keys or queries, are 0."""
+    Hq, Tq, _ = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0 or k1 == k0:
+            continue
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            dq[hs, q0:q1], dk[g, k0:k1], dv[g, k0:k1] = attn_bwd_group(
+                q[hs, q0:q1], k[g, k0:k1], v[g, k0:k1], do[hs, q0:q1], scale, causal)
+    return dq, dk, dv

@@ -40,6 +40,7 @@ def make_ns(att, fold):
         fold_head=fold.fold_head,
         merge_partials=att.merge_partials,
         attn_fwd_varlen=att.attn_fwd_varlen,
+        attn_bwd_varlen=att.attn_bwd_varlen,
     )
 
 
@@ -455,6 +456,88 @@ def pin_varlen(ns):
                 _close(O[hq, q0:q1], Ob, TOL, f"varlen O seq={b} hq={hq} causal={causal}")
                 _close_inf(l[hq, q0:q1], Lb, TOL, f"varlen lse seq={b} hq={hq} causal={causal}")
 
+def _num_grad(loss, arrays, h=1e-6):
+    """Central differences of loss() with respect to every element of every
+    array in `arrays` (edited in place and restored)."""
+    out = []
+    for arr in arrays:
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            x0 = arr[idx]
+            arr[idx] = x0 + h
+            lp = loss()
+            arr[idx] = x0 - h
+            lm = loss()
+            arr[idx] = x0
+            num[idx] = (lp - lm) / (2 * h)
+        out.append(num)
+    return out
+
+
+def pin_bwd_rectangular(ns):
+    """Nq != Nk (bottom-right causal mask), a group of two query heads: the
+    analytic gradients of L = sum(dO * O) agree with central differences of
+    the forward definition; with Nq > Nk the first Nq - Nk query rows see no
+    key (O = 0 for any input), so their dq is exactly 0; sum_j dK_j = 0."""
+    sc = 0.6
+    for Nq, Nk in ((5, 9), (9, 5)):
+        G, d = 2, 3
+        q = _rand((G, Nq, d), 61)
+        k = _rand((Nk, d), 62)
+        v = _rand((Nk, d), 63)
+        do = _rand((G, Nq, d), 64)
+        for causal in (False, True):
+            dq, dk, dv = ns.attn_bwd_group(q, k, v, do, sc, causal)
+
+            def loss():
+                return sum(float(np.sum(do[j] * ns.attn_fwd_head(q[j], k, v, sc, causal)[0])) for j in range(G))
+
+            for got, num, name in zip((dq, dk, dv), _num_grad(loss, [q, k, v]), ("dq", "dk", "dv")):
+                _close(got, num, 1e-7, f"rectangular Nq={Nq} Nk={Nk} {name} causal={causal}")
+            _close(dk.sum(axis=0), np.zeros(d), 1e-12, f"rectangular sum dK Nq={Nq} Nk={Nk} causal={causal}")
+            if causal and Nq > Nk:
+                assert np.all(dq[:, : Nq - Nk] == 0.0), "rows without keys have dq = 0"
+
+
+def pin_bwd_varlen(ns):
+    """Variable-length batch (GQA, sequences with no queries, no keys, fewer
+    and more queries than keys): the analytic gradients agree with central
+    differences of the packed forward definition; per sequence and K/V head
+    sum_j dK_j = 0 and sum_j dV_j = the sum of dO over the group's query rows
+    that see a key; rows of sequences without keys or queries are 0."""
+    sc = 0.5
+    cu_q = [0, 3, 3, 8, 10, 14]
+    cu_k = [0, 5, 9, 9, 16, 18]
+    Hq, Hkv, d = 4, 2, 3
+    G = Hq // Hkv
+    q = _rand((Hq, cu_q[-1], d), 65)
+    k = _rand((Hkv, cu_k[-1], d), 66)
+    v = _rand((Hkv, cu_k[-1], d), 67)
+    do = _rand((Hq, cu_q[-1], d), 68)
+    for causal in (False, True):
+        dq, dk, dv = ns.attn_bwd_varlen(q, k, v, do, cu_q, cu_k, sc, causal)
+
+        def loss():
+            return float(np.sum(do * ns.attn_fwd_varlen(q, k, v, cu_q, cu_k, sc, causal)[0]))
+
+        for got, num, name in zip((dq, dk, dv), _num_grad(loss, [q, k, v]), ("dq", "dk", "dv")):
+            _close(got, num, 1e-7, f"varlen {name} causal={causal}")
+        for b in range(len(cu_q) - 1):
+            q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            nq, nk = q1 - q0, k1 - k0
+            for g in range(Hkv):
+                _close(dk[g, k0:k1].sum(axis=0), np.zeros(d), 1e-12, f"varlen sum dK seq={b} g={g}")
+                seen = np.arange(nq) + (nk - nq if causal else nk) >= 0 if nk else np.zeros(nq, bool)
+                expect = do[g * G:(g + 1) * G, q0:q1][:, seen].sum(axis=(0, 1)) if nk else np.zeros(d)
+                _close(dv[g, k0:k1].sum(axis=0), expect, 1e-12, f"varlen sum dV seq={b} g={g} causal={causal}")
+            if nk == 0:
+                assert np.all(dq[:, q0:q1] == 0.0), f"seq {b} without keys: dq = 0"
+            if nq == 0:
+                assert np.all(dk[:, k0:k1] == 0.0) and np.all(dv[:, k0:k1] == 0.0), f"seq {b} without queries"
+
+
 FWD_PINS = [
     pin_fold_equals_definition,
     pin_rows_sum_to_one,
@@ -472,5 +555,7 @@ BWD_PINS = [
     pin_bwd_finite_difference,
     pin_bwd_invariants,
     pin_bwd_qzero_causal,
+    pin_bwd_rectangular,
+    pin_bwd_varlen,
 ]
 ALL_PINS = FWD_PINS + BWD_PINS

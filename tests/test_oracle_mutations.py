@@ -51,9 +51,20 @@ MUTATIONS = [
      "w = np.where(np.isfinite(lse_parts[s_]), 1.0, 0.0)"),
     ("merge_no_divide", ATT, "o / np.where(seen, l, 1.0)[:, None], 0.0), m + np.log(l)",
      "o, 0.0), m + np.log(l)"),
-    ("varlen_key_rows", ATT, "k[g, k0:k1], v[g, k0:k1]", "k[g, q0:q1], v[g, q0:q1]"),
+    ("varlen_key_rows", ATT, "attn_fwd_head(q[hq, q0:q1], k[g, k0:k1], v[g, k0:k1]",
+     "attn_fwd_head(q[hq, q0:q1], k[g, q0:q1], v[g, q0:q1]"),
     ("fold_offset_dropped", FOLD, "<= qi[:, None] + offset", "<= qi[:, None]"),
     ("fold_range_from_zero", FOLD, "range(key_lo, key_hi, block_k)", "range(0, key_hi, block_k)"),
+    ("bwd_offset_dropped", ATT, "vis = _visible(np.arange(Nq), Nk, causal, Nk - Nq)",
+     "vis = _visible(np.arange(Nq), Nk, causal, 0)"),
+    ("bwd_offset_sign", ATT, "vis = _visible(np.arange(Nq), Nk, causal, Nk - Nq)",
+     "vis = _visible(np.arange(Nq), Nk, causal, Nq - Nk)"),
+    ("bwd_varlen_key_rows", ATT, "q[hs, q0:q1], k[g, k0:k1], v[g, k0:k1], do[hs, q0:q1]",
+     "q[hs, q0:q1], k[g, q0:q1], v[g, q0:q1], do[hs, q0:q1]"),
+    ("bwd_varlen_heads_interleaved", ATT, "            hs = slice(g * G, (g + 1) * G)\n            dq[hs, q0:q1]",
+     "            hs = slice(g, Hq, Hkv)\n            dq[hs, q0:q1]"),
+    ("bwd_varlen_do_rows", ATT, "v[g, k0:k1], do[hs, q0:q1], scale, causal)",
+     "v[g, k0:k1], do[hs, k0:k0 + (q1 - q0)], scale, causal)"),
     ("fold_wrong_scale", FOLD, "s = scale * (qr @ k_h[j0:j1].T)", "s = scale * scale * (qr @ k_h[j0:j1].T)"),
 ]
 
