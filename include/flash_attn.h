@@ -200,22 +200,18 @@ size_t flash_attn_naive_workspace_bytes(int B, int Hq, int N);
 
 /*
  * Bytes of device workspace flash_attn_bwd / flash_attn_bwd_f32 need for these
- * sizes: per query row two fp32 (D_i = sum_c dO_ic O_ic, and lse_i * log2(e))
- * and d fp32 (the accumulator the bf16 backward sums dQ in, over key blocks):
- * 2*A(4R) + A(4*R*d) bytes with R = B*Hq*N and A() rounding up to a multiple
- * of 256. Linear in N: no N x N buffer. Returns 0 for invalid sizes.
+ * sizes: two fp32 per query row (D_i = sum_c dO_ic O_ic, and lse_i * log2(e)),
+ * 2*A(4R) bytes with R = B*Hq*N and A() rounding up to a multiple of 256.
+ * Linear in N: no N x N buffer. Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
 /*
  * Backward, bf16 storage, fp32 accumulation. Recomputes every score block from
- * q, k and the forward's lse; returns the gradients of sum(dout * O). For
- * d <= 128 every score block is recomputed once and gives dK, dV and its
- * share of dQ (five products per pair of blocks); the shares of dQ are added
- * into the workspace's fp32 accumulator with atomic adds, in an order that
- * varies from run to run, so dq may differ in its last bits between runs
- * (dk and dv do not). At d = 256 dQ comes from a second kernel that
- * recomputes the scores (seven products) and all outputs are repeatable.
+ * q, k and the forward's lse; returns the gradients of sum(dout * O). dK and
+ * dV come from a pass over the query blocks of each key block, dQ from a pass
+ * over the key blocks of each query block, which recomputes the scores once
+ * more; no atomics, so every run gives the same bits.
  *   q, o, dout [B,Hq,N,d], k, v [B,Hkv,N,d] (bf16 bits), lse [B,Hq,N] fp32:
  *     the forward's inputs and outputs (o and lse exactly as flash_attn_fwd
  *     returned them for the same q, k, v, scale, causal).
@@ -229,6 +225,39 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * General backward, bf16 storage: the gradients of the general forward's
+ * problems (flash_attn_fwd_kv / flash_attn_fwd_varlen without split keys),
+ * computed as flash_attn_bwd computes them:
+ *   - Nq queries and Nk keys per sequence, the causal mask aligned to the
+ *     bottom right (query i sees key j iff j <= i + Nk - Nq). A query that
+ *     sees no key (O = 0, lse = -inf) has dq = 0 and adds nothing to dk, dv.
+ *   - o and lse exactly as the forward returned them.
+ * flash_attn_bwd_kv: q, o, dout, dq [B,Hq,Nq,d]; k, v, dk, dv [B,Hkv,Nk,d]
+ *   (bf16 bits); lse [B,Hq,Nq] fp32.
+ * flash_attn_bwd_varlen: B sequences packed along the token axis, the layout
+ *   and cu_seqlens conventions of flash_attn_fwd_varlen: q, o, dout, dq
+ *   [Hq,Tq,d]; k, v, dk, dv [Hkv,Tk,d]; lse [Hq,Tq]. A sequence without keys
+ *   gets dq = 0, one without queries dk = dv = 0; rows outside every
+ *   sequence, and rows beyond max_seqlen_q / max_seqlen_k in a sequence, are
+ *   left unspecified.
+ * workspace, workspace_bytes: caller-owned device buffer of at least
+ *   flash_attn_bwd_kv_workspace_bytes(rows, d) bytes, rows = B*Hq*Nq
+ *   (uniform) or Hq*Tq (varlen); contents on entry ignored, on return
+ *   unspecified.
+ * Errors as flash_attn_fwd_kv; FA_ERR_WORKSPACE for a missing or short
+ * workspace.
+ */
+size_t flash_attn_bwd_kv_workspace_bytes(long long rows, int d);
+int flash_attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream);
+int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                          const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                          int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                          void* stream);
 
 /* Backward, fp32 check mode: as flash_attn_bwd with fp32 tensors. */
 int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

@@ -34,6 +34,11 @@ __all__ = [
     "flash_attn_naive_workspace_bytes",
     "attention_forward_varlen",
     "attention_backward",
+    "flash_attn_bwd_kv",
+    "flash_attn_bwd_varlen",
+    "flash_attn_bwd_kv_workspace_bytes",
+    "attention_backward_kv",
+    "attention_backward_varlen",
 ]
 
 _LIB = None
@@ -87,6 +92,12 @@ def load_library():
     lib.flash_attn_naive_fwd.restype = I
     lib.flash_attn_naive_workspace_bytes.argtypes = [I, I, I]
     lib.flash_attn_naive_workspace_bytes.restype = Z
+    lib.flash_attn_bwd_kv.argtypes = [P] * 10 + [Z] + [I] * 6 + [F, I, P]
+    lib.flash_attn_bwd_kv.restype = I
+    lib.flash_attn_bwd_varlen.argtypes = [P] * 12 + [Z] + [I] * 8 + [F, I, P]
+    lib.flash_attn_bwd_varlen.restype = I
+    lib.flash_attn_bwd_kv_workspace_bytes.argtypes = [L, I]
+    lib.flash_attn_bwd_kv_workspace_bytes.restype = Z
     lib.flash_attn_status_str.argtypes = [I]
     lib.flash_attn_status_str.restype = ctypes.c_char_p
     _LIB = lib
@@ -392,3 +403,78 @@ def flash_attn_naive_fwd(q, k, v, o, lse, scale, causal, workspace, stream=None)
                                              _stream(stream))
     if st != 0:
         raise FlashAttnError("flash_attn_naive_fwd", st)
+
+
+def flash_attn_bwd_kv_workspace_bytes(rows, d) -> int:
+    return int(load_library().flash_attn_bwd_kv_workspace_bytes(int(rows), int(d)))
+
+
+def _check_grads(q, k, dout, dq, dk, dv):
+    for what, t in (("dout", dout), ("dq", dq)):
+        _expect_shape(what, t, tuple(q.shape))
+    for what, t in (("dk", dk), ("dv", dv)):
+        _expect_shape(what, t, tuple(k.shape))
+
+
+def flash_attn_bwd_kv(q, k, v, o, lse, dout, dq, dk, dv, workspace, scale, causal, stream=None):
+    """bf16 backward of flash_attn_fwd_kv's problem (Nq queries, Nk keys,
+    bottom-right causal) into caller-allocated dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _check_kv_shapes(q, k, v, o, lse)
+    _check_grads(q, k, dout, dq, dk, dv)
+    _check(q, k, v, o, dout, dq, dk, dv, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    _check(workspace)
+    need = flash_attn_bwd_kv_workspace_bytes(B * Hq * Nq, d)
+    if _ws_size(workspace) < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    st = load_library().flash_attn_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(workspace), _ws_size(workspace), B, Hq, Hkv, Nq,
+                                          Nk, d, float(scale), int(bool(causal)), _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_bwd_kv", st)
+
+
+def flash_attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          workspace, scale, causal, stream=None):
+    """bf16 backward of flash_attn_fwd_varlen's problem: q, o, dout, dq [Hq,Tq,d],
+    k, v, dk, dv [Hkv,Tk,d], lse [Hq,Tq] fp32, cu_seqlens_* int32 [B+1] on the GPU."""
+    import torch
+    B, Hq, Hkv, Tq, Tk, d = _check_varlen_shapes(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k)
+    _check_grads(q, k, dout, dq, dk, dv)
+    _check(q, k, v, o, dout, dq, dk, dv, dtype=torch.bfloat16)
+    _check(lse, dtype=torch.float32)
+    _check(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    _check(workspace)
+    need = flash_attn_bwd_kv_workspace_bytes(Hq * Tq, d)
+    if _ws_size(workspace) < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    st = load_library().flash_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                              _ptr(workspace), _ws_size(workspace), B, Hq, Hkv, Tq, Tk,
+                                              int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
+                                              int(bool(causal)), _stream(stream))
+    if st != 0:
+        raise FlashAttnError("flash_attn_bwd_varlen", st)
+
+
+def attention_backward_kv(q, k, v, o, lse, dout, scale, causal, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run flash_attn_bwd_kv."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, Hq, Nq, d = (int(x) for x in q.shape)
+    ws = torch.empty(max(flash_attn_bwd_kv_workspace_bytes(B * Hq * Nq, d), 256), dtype=torch.uint8, device=q.device)
+    flash_attn_bwd_kv(q, k, v, o, lse, dout, dq, dk, dv, ws, scale, causal, stream)
+    return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                              causal, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run flash_attn_bwd_varlen."""
+    import torch
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    Hq, Tq, d = (int(x) for x in q.shape)
+    ws = torch.empty(max(flash_attn_bwd_kv_workspace_bytes(Hq * Tq, d), 256), dtype=torch.uint8, device=q.device)
+    flash_attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          ws, scale, causal, stream)
+    return dq, dk, dv

@@ -57,6 +57,45 @@ int fwd_common(bool f32, const void* q, const void* k, const void* v, void* o, f
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Arguments of the bf16 backward; the workspace holds D then l2.
+fa::BwdKvArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, const int* cu_q, const int* cu_k,
+                       void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int max_nq, int max_nk,
+                       long long rows, float scale) {
+  fa::BwdKvArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = static_cast<float*>(workspace);
+  a.l2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + fa::bwd_ws_l2_offset(rows));
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.max_nq = max_nq;
+  a.max_nk = max_nk;
+  a.rows = rows;
+  a.c = scale * kLog2e;
+  a.scale = scale;
+  return a;
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
+  if (workspace == nullptr) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
 int bwd_common(bool f32, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
@@ -64,44 +103,53 @@ int bwd_common(bool f32, const void* q, const void* k, const void* v, const void
   int st = check_ptrs(ptrs, 9);
   if (st == FA_OK) st = check_shape(B, Hq, Hkv, N, d, causal);
   if (st == FA_OK) st = check_scale(scale);
+  if (st == FA_OK) st = check_workspace(workspace, workspace_bytes, flash_attn_bwd_workspace_bytes(B, Hq, Hkv, N, d));
   if (st != FA_OK) return st;
-  if (workspace == nullptr) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  if (workspace_bytes < flash_attn_bwd_workspace_bytes(B, Hq, Hkv, N, d)) return FA_ERR_WORKSPACE;
-  const float c = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* dsum = static_cast<float*>(workspace);
   hipError_t e;
   if (f32) {
-    e = fa::bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
-  } else if (d <= 128) {
-    // One pass over the score blocks (dK, dV and dQ together).
-    fa::BwdKvArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
-    a.dout = dout;
-    a.dq = dq;
-    a.dk = dk;
-    a.dv = dv;
-    const long long rows = (long long)B * Hq * N;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    a.dsum = dsum;
-    a.l2 = reinterpret_cast<float*>(ws + fa::bwd_ws_l2_offset(rows));
-    a.dqa = reinterpret_cast<float*>(ws + fa::bwd_ws_dqa_offset(rows));
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.Nq = a.Nk = a.max_nq = a.max_nk = N;
-    a.rows = rows;
-    a.c = c;
-    a.scale = scale;
-    e = fa::bwd_fused_bf16(a, d, causal, s);
+    e = fa::bwd_f32(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, N, d, scale,
+                    scale * kLog2e, causal, s);
   } else {
-    e = fa::bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, N, d, scale, c, causal, s);
+    const fa::BwdKvArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, workspace, B, Hq, Hkv, N, N,
+                                     N, N, (long long)B * Hq * N, scale);
+    e = fa::bwd_bf16(a, d, causal, s);
   }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// Shape checks of the general forward and backward: positive sizes, Hq a
+// multiple of Hkv, supported d, element offsets within 2^40, grids within
+// int32 (the backward's key blocks are 64 keys at the smallest).
+int check_kv_shape(int B, int Hq, int Hkv, int Nq, int Nk, int max_nq, int max_nk, int d, int causal,
+                   bool varlen) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Nq <= 0 || Nk <= 0 || max_nq <= 0 || max_nk <= 0)
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  const long long rows = varlen ? (long long)Hq * Nq : (long long)B * Hq * Nq;
+  const long long krows = varlen ? (long long)Hkv * Nk : (long long)B * Hkv * Nk;
+  if (rows * d > ((long long)1 << 40) || krows * d > ((long long)1 << 40)) return FA_ERR_SHAPE;
+  if (((long long)max_nk + 63) / 64 * Hkv * B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (((long long)max_nq + 31) / 32 * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int bwd_kv_common(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, const int* cu_q, const int* cu_k, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int max_nq, int max_nk, int d,
+                  float scale, int causal, void* stream) {
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  int st = check_ptrs(ptrs, 9);
+  if (st == FA_OK) st = check_kv_shape(B, Hq, Hkv, Nq, Nk, max_nq, max_nk, d, causal, cu_q != nullptr);
+  if (st == FA_OK) st = check_scale(scale);
+  const long long rows = cu_q ? (long long)Hq * Nq : (long long)B * Hq * Nq;
+  if (st == FA_OK) st = check_workspace(workspace, workspace_bytes, fa::bwd_ws_bytes(rows));
+  if (st != FA_OK) return st;
+  const fa::BwdKvArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, workspace, B, Hq, Hkv, Nq, Nk,
+                                   max_nq, max_nk, rows, scale);
+  const hipError_t e = fa::bwd_bf16(a, d, causal, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -237,9 +285,9 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
 
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_shape(B, Hq, Hkv, N, d, 0) != FA_OK) return 0;
-  // D (fp32 per query row), lse * log2(e) (fp32 per query row) and the fp32
-  // dQ accumulator (d per query row), each from a 256-byte boundary.
-  return fa::bwd_ws_bytes((long long)B * Hq * N, d);
+  // D (fp32 per query row), then lse * log2(e) (fp32 per query row) from the
+  // next 256-byte boundary.
+  return fa::bwd_ws_bytes((long long)B * Hq * N);
 }
 
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -254,6 +302,28 @@ int flash_attn_bwd_f32(const float* q, const float* k, const float* v, const flo
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* stream) {
   return bwd_common(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d, scale,
                     causal, stream);
+}
+
+size_t flash_attn_bwd_kv_workspace_bytes(long long rows, int d) {
+  if (rows <= 0 || (d != 64 && d != 128 && d != 256)) return 0;
+  return fa::bwd_ws_bytes(rows);
+}
+
+int flash_attn_bwd_kv(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  return bwd_kv_common(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, workspace, workspace_bytes, B, Hq, Hkv,
+                       Nq, Nk, Nq, Nk, d, scale, causal, stream);
+}
+
+int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                          const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                          int Tq, int Tk, int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                          void* stream) {
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERR_NULL;
+  return bwd_kv_common(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, workspace, workspace_bytes, B,
+                       Hq, Hkv, Tq, Tk, max_seqlen_q, max_seqlen_k, d, scale, causal, stream);
 }
 
 int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {

@@ -1,17 +1,37 @@
 // Backward kernels, bf16 storage: the throughput path of the gradients.
 //
-// Same method and the same three launches as fa_bwd.hpp (the gradients of
-// exact softmax attention, every score block recomputed from Q, K and the
-// forward's lse: fanfani.net "FlashAttention", section "The backward pass, and
-// where the memory saving comes from"; synthetic.wiki "FlashAttention:
-// attention's bottleneck is the wire, not the maths", section "The backward
-// pass buys memory with recompute"). What differs is how data reaches the
-// matrix cores on gfx950:
+// The gradients of exact softmax attention with every score block recomputed
+// from Q, K and the forward's lse (fanfani.net "FlashAttention", section "The
+// backward pass, and where the memory saving comes from"; synthetic.wiki
+// "FlashAttention: attention's bottleneck is the wire, not the maths",
+// section "The backward pass buys memory with recompute"), in three launches:
 //
-//  * The streamed tiles (Q and dO in the dK/dV kernel, K and V in the dQ
-//    kernel) go from global memory straight into LDS (global_load_lds),
-//    double-buffered: block i+1 is in flight while block i is computed, one
-//    barrier per block of 64 rows.
+//  1. bwd_prep_bf16_kernel: D_i = dO_i . O_i and l2_i = lse_i * log2(e) per
+//     query row, into the caller's workspace (so that P = exp2(s*c - l2)
+//     costs one fma and one exp per score).
+//  2. bwd_dkdv_bf16_kernel: one workgroup per (key block, K/V head,
+//     sequence): S, P, dP, dS of every visible query block, dV += P^T dO and
+//     dK += dS^T Q (four products per pair of blocks).
+//  3. bwd_dq_bf16_kernel: one workgroup per (query block, query head,
+//     sequence): S, P, dP, dS again and dQ += dS K (three products).
+//
+// Seven products per pair of blocks instead of the five the method needs:
+// the alternative, dQ summed over key blocks by fp32 atomic adds from kernel
+// 2, was built and measured on MI355X and is slower here (the atomic traffic,
+// one fp32 dQ tile per pair of blocks, runs at about 2.7 TB/s; at B=1, H=32,
+// N=8192 that is 4.4 GB, 1.6 ms against 0.6 ms for kernel 3).
+//
+// Shapes: Nq queries and Nk keys per sequence, the causal mask aligned to the
+// bottom right (query i sees key j iff j <= i + Nk - Nq; a row that sees no
+// key has O = 0, lse = -inf and zero gradients), uniform [B, H, N, d]
+// batches or variable-length sequences packed along the token axis ([H, T,
+// d] with cu_seqlens), as the general forward (fa_fwd_kv_bf16.hpp). The
+// square backward is the case Nq = Nk.
+//
+// How the data reaches the matrix cores on gfx950:
+//  * The streamed tiles (Q and dO in kernel 2, K and V in kernel 3) go from
+//    global memory straight into LDS (global_load_lds), double-buffered:
+//    block i+1 is in flight while block i is computed.
 //  * Each tile is stored once, row-major, with rows padded by 16 bytes, and is
 //    read two ways: 16-byte row reads where it is contracted over d (Q K^T,
 //    dO V^T) and transposing reads (ds_read_b64_tr_b16) where it is contracted
@@ -22,8 +42,6 @@
 //    16-lane group gathers in a transposing read are 4 rows apart, so with
 //    16-byte padding both kinds of read are bank-conflict free, and (c) every
 //    fragment address is a fixed offset from one per-lane base.
-//  * The preprocess also stores lse * log2(e) next to D, so P = exp2(s*c - l2)
-//    costs one fma and one exp per score.
 #pragma once
 
 #include "fa_bwd.hpp"
@@ -41,29 +59,6 @@ __device__ __forceinline__ constexpr int rho(int i) {
 // when the tile's rows were taken in rho order: rho(8*(r/4) + 4*h + r%4).
 __device__ __forceinline__ constexpr int rho_row(int r, int h) {
   return 16 * (r >> 3) + 4 * (r & 3) + 2 * ((r >> 2) & 1) + h;
-}
-
-// D_i = dO_i . O_i and l2_i = lse_i * log2(e), one row per D/8 threads.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdArgs a, float* l2) {
-  constexpr int TPR = D / 8;
-  constexpr int RPB = 256 / TPR;
-  const long long rows = (long long)a.B * a.Hq * a.N;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 of = global_frag<uint16_t>(static_cast<const uint16_t*>(a.o) + row * D + part * 8);
-    const bf16x8 gf = global_frag<uint16_t>(static_cast<const uint16_t*>(a.dout) + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)of[e], (float)gf[e], acc);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) {
-    a.dsum[row] = acc;
-    l2[row] = a.lse[row] * kLog2eF;
-  }
 }
 
 // Direct copy of 64 per-row fp32 values (rows r0 .. r0+63 of one head, taken
@@ -87,8 +82,8 @@ __device__ __forceinline__ void dma_row_stats(uint8_t* lds, const float* g, int 
 }
 
 // Workgroup barrier that orders LDS accesses only: waits for this wave's own
-// LDS operations (lgkmcnt), not for its global loads, direct-to-LDS copies or
-// atomics in flight, which a plain __syncthreads() would also wait for.
+// LDS operations (lgkmcnt), not for its global loads or direct-to-LDS copies
+// in flight, which a plain __syncthreads() would also wait for.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -102,7 +97,52 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int rows_apart_bytes
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// dK and dV: one workgroup per (block of 32*NP keys, K/V head, batch), with
+// The extent of sequence b: query rows qs .. qs+nq-1 and key rows ks ..
+// ks+nk-1 of each head, and the row strides of the batch and head axes.
+struct SeqExtent {
+  int qs, nq, ks, nk;
+  long long q_bs, q_hs, k_bs, k_hs;
+  __device__ __forceinline__ long long qrow0(int b, int hq) const { return b * q_bs + hq * q_hs + qs; }
+  __device__ __forceinline__ long long krow0(int b, int hkv) const { return b * k_bs + hkv * k_hs + ks; }
+};
+__device__ __forceinline__ SeqExtent seq_extent(const BwdKvArgs& a, int b) {
+  SeqExtent e{0, a.Nq, 0, a.Nk, (long long)a.Hq * a.Nq, a.Nq, (long long)a.Hkv * a.Nk, a.Nk};
+  if (a.cu_q != nullptr) {
+    // Offsets clamped into [0, total], lengths to the grid's maximum: any
+    // offsets keep every access in bounds.
+    e.qs = min(max(a.cu_q[b], 0), a.Nq);
+    e.nq = min(min(max(a.cu_q[b + 1], e.qs), a.Nq) - e.qs, a.max_nq);
+    e.ks = min(max(a.cu_k[b], 0), a.Nk);
+    e.nk = min(min(max(a.cu_k[b + 1], e.ks), a.Nk) - e.ks, a.max_nk);
+    e.q_bs = 0;
+    e.k_bs = 0;
+  }
+  return e;
+}
+
+// D = dO . O and l2 = lse * log2(e) per query row; one row per D/8 threads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdKvArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < a.rows) {
+    const bf16x8 of = global_frag<uint16_t>(static_cast<const uint16_t*>(a.o) + row * D + part * 8);
+    const bf16x8 gf = global_frag<uint16_t>(static_cast<const uint16_t*>(a.dout) + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)of[e], (float)gf[e], acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < a.rows && part == 0) {
+    a.dsum[row] = acc;
+    a.l2[row] = a.lse[row] * kLog2eF;
+  }
+}
+
+// dK and dV: one workgroup per (block of 32*NP keys, K/V head, sequence), with
 // 2*NP waves in NP pairs; pair p owns keys k0 + 32p .. +31 and splits the
 // work of each 32-query subtile between its two waves:
 //   wave p      ("P wave"):  S = Q K^T, P = exp2(S*c - l2) (masked), P -> LDS,
@@ -113,10 +153,11 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* p, int rows_apart_bytes
 // the pair's registers, so two waves fit on each SIMD and the softmax work of
 // one overlaps the products of the other. Per block of 64 queries: barrier 1
 // (block landed, previous block done), the P waves write P, barrier 2 (P
-// visible), the products that need P. Q, dO, l2 and D stream through LDS in
-// double-buffered blocks. No atomics: deterministic.
+// visible; LDS only, the next block's copies stay in flight), the products
+// that need P. Q, dO, l2 and D stream through LDS in double-buffered blocks,
+// over every query head of the K/V head's group. No atomics: deterministic.
 template <int D, int NP, bool CAUSAL>
-__global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, const float* l2g) {
+__global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
   constexpr int NW = 2 * NP;
   constexpr int BKV = 32 * NP, BQ = 64;
   constexpr int RS = 2 * D + 16;  // padded LDS row bytes
@@ -127,55 +168,59 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + NP * PX];
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-  const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool pwave = wave < NP;
   const int pair = pwave ? wave : wave - NP;
   const int h = lane >> 5, li = lane & 31;
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int nkb = (N + BKV - 1) / BKV;
-  int b, hkv, kb;
-  decode_block(blockIdx.x, a.Hkv, a.B, nkb, false, b, hkv, kb);  // key block 0 has the most work
   const int G = a.Hq / a.Hkv;
+  const int nkb_max = (a.max_nk + BKV - 1) / BKV;
+  int b, hkv, kb;
+  decode_block(blockIdx.x, a.Hkv, a.B, nkb_max, false, b, hkv, kb);  // key block 0 has the most work
+  const SeqExtent sq = seq_extent(a, b);
+  const int nq = sq.nq, nk = sq.nk;
   const int k0 = kb * BKV;
+  if (k0 >= nk) return;  // uniform over the workgroup: no barrier reached yet
+  const int off = CAUSAL ? nk - nq : 0;  // causal: query i sees key j iff j <= i + off
   const int kw0 = k0 + pair * 32;
   const int kj = kw0 + li;  // this lane's key
+  const long long krow0 = sq.krow0(b, hkv);
 
-  const size_t kvoff = (size_t)(b * a.Hkv + hkv) * N * D;
-
-  // Q, dO, l2, D of step i (query head g = i / nq, query block qb_start + i % nq).
-  const int nqb = (N + BQ - 1) / BQ;
-  const int qb_start = CAUSAL ? k0 / BQ : 0;
-  const int nq = nqb - qb_start;
-  const int nsteps = G * nq;
+  // Steps: (query head g of the group, query block), from the first query
+  // block any key of this workgroup is visible to. A sequence without
+  // queries has no steps: its dK and dV are 0.
+  const int nqb = (nq + BQ - 1) / BQ;
+  const int qb_start = CAUSAL ? max(0, k0 - off) / BQ : 0;
+  const int nqs = nq > 0 ? max(nqb - qb_start, 0) : 0;
+  const int nsteps = G * nqs;
   BlockDma<D, BQ, RS, NW> dma;
   dma.init(wave, lane);
   auto prefetch = [&](int i) {
-    const int g = i / nq, q0 = (qb_start + i % nq) * BQ;
-    const size_t qoff = (size_t)(b * a.Hq + hkv * G + g) * N;
+    const int g = i / nqs, q0 = (qb_start + i % nqs) * BQ;
+    const long long qr = sq.qrow0(b, hkv * G + g);
     uint8_t* st = smem + (i & 1) * STAGE;
-    const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + (qoff + q0) * D;
-    const uint16_t* Og = static_cast<const uint16_t*>(a.dout) + (qoff + q0) * D;
-    if (q0 + BQ <= N) {
+    const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + (qr + q0) * D;
+    const uint16_t* Og = static_cast<const uint16_t*>(a.dout) + (qr + q0) * D;
+    if (q0 + BQ <= nq) {
       dma.template issue<true>(st, Qg, BQ, wave);
       dma.template issue<true>(st + TILE, Og, BQ, wave);
     } else {
-      dma.template issue<false>(st, Qg, N - q0, wave);
-      dma.template issue<false>(st + TILE, Og, N - q0, wave);
+      dma.template issue<false>(st, Qg, nq - q0, wave);
+      dma.template issue<false>(st + TILE, Og, nq - q0, wave);
     }
-    if (wave == 0) dma_row_stats(st + 2 * TILE, l2g + qoff, q0, N, lane);
-    if (wave == NW - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qoff, q0, N, lane);
+    if (wave == 0) dma_row_stats(st + 2 * TILE, a.l2 + qr, q0, nq, lane);
+    if (wave == NW - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qr, q0, nq, lane);
   };
   if (nsteps > 0) prefetch(0);
 
   // This wave's resident operand: K (P wave) or V (dS wave), 32 keys, as
   // B-operand fragments; and its accumulator, dV^T or dK^T.
-  const uint16_t* KV = static_cast<const uint16_t*>(pwave ? a.k : a.v) + kvoff;
+  const uint16_t* KV = static_cast<const uint16_t*>(pwave ? a.k : a.v) + krow0 * D;
   bf16x8 kvf[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
-    kvf[f] = (kj < N) ? global_frag<uint16_t>(KV + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    kvf[f] = (kj < nk) ? global_frag<uint16_t>(KV + (size_t)kj * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = zero16();
@@ -192,22 +237,22 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // barrier 1: step i has landed; every wave is done with step i-1
     if (i + 1 < nsteps) prefetch(i + 1);
-    const int q0 = (qb_start + i % nq) * BQ;
+    const int q0 = (qb_start + i % nqs) * BQ;
     const uint8_t* st = smem + (i & 1) * STAGE;
     const float* l2s = reinterpret_cast<const float*>(st + 2 * TILE);
     const float* dss = l2s + BQ;
-    // Subtile sub (queries q0 + 32 sub ..) is needed unless it is past N or
+    // Subtile sub (queries q0 + 32 sub ..) is needed unless it is past nq or
     // (causal) every key of the pair follows every query of it.
-    const bool need0 = !CAUSAL || q0 + 31 >= kw0;
-    const bool need1 = q0 + 32 < N && (!CAUSAL || q0 + 63 >= kw0);
+    const bool need0 = !CAUSAL || q0 + 31 + off >= kw0;
+    const bool need1 = q0 + 32 < nq && (!CAUSAL || q0 + 63 + off >= kw0);
     // Both roles run the same products on role-selected tiles, so that the
     // accumulators stay in one set of registers:
     //   x = rows . kvf:     S = Q K^T (P wave) or dP = dO V^T (dS wave);
     //   acc += tr . bfr:    dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
-    const uint8_t* qs = st;
-    const uint8_t* os = st + TILE;
-    const uint8_t* rows = pwave ? qs : os;
-    const uint8_t* trs = pwave ? os : qs;
+    const uint8_t* qsm = st;
+    const uint8_t* osm = st + TILE;
+    const uint8_t* rows = pwave ? qsm : osm;
+    const uint8_t* trs = pwave ? osm : qsm;
     // The products of a subtile are issued even when it is not needed (its
     // rows are in LDS either way; the result is then not used), so that in
     // the P wave subtile 1's products and subtile 0's exponentials sit in
@@ -235,13 +280,15 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
 #pragma unroll
           for (int e = 0; e < 4; ++e) p[4 * r4 + e] = __builtin_amdgcn_exp2f(fmaf(x[sub][4 * r4 + e], c, -l4[e]));
         }
-        // Masks: query row >= N, or (causal) key > query.
-        if ((CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N) {
-          const int kd = kj - qs0 - h, nd = N - qs0 - h;
+        // Masks: query row >= nq, key >= nk, or (causal) key > query + off.
+        // A query that sees no key (lse = -inf) is masked on every key.
+        if ((CAUSAL && qs0 + off < kw0 + 31) || qs0 + 32 > nq || kw0 + 32 > nk) {
+          const int kd = kj - off - qs0 - h, nd = nq - qs0 - h;
+          const bool kout = kj >= nk;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int base = rho_row(r, 0);
-            if ((CAUSAL && kd > base) || nd <= base) p[r] = 0.f;
+            if ((CAUSAL && kd > base) || nd <= base || kout) p[r] = 0.f;
           }
         }
 #pragma unroll
@@ -283,9 +330,9 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
     }
   }
 
-  if (kj < N) {
+  if (kj < nk) {
     // P waves hold dV^T, dS waves dK^T (times scale): rows = d, column = key li.
-    uint16_t* out = static_cast<uint16_t*>(pwave ? a.dv : a.dk) + kvoff + (size_t)kj * D;
+    uint16_t* out = static_cast<uint16_t*>(pwave ? a.dv : a.dk) + (krow0 + kj) * D;
     const float mul = pwave ? 1.f : a.scale;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
@@ -299,12 +346,12 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdArgs a, cons
   }
 }
 
-// dQ: one workgroup per (block of 32*NW queries, query head, batch). Each wave
-// keeps 32 query rows of Q and dO as B-operand fragments in registers and
+// dQ: one workgroup per (block of 32*NW queries, query head, sequence). Each
+// wave keeps 32 query rows of Q and dO as B-operand fragments in registers and
 // accumulates dQ^T over the visible key blocks; K and V stream through LDS in
 // blocks of 64 keys.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const float* l2g) {
+__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
   constexpr int BM = 32 * NW, BK = 64;
   constexpr int RS = 2 * D + 16;
   constexpr int NF = D / 16, NDT = D / 32;
@@ -312,42 +359,48 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
   constexpr int STAGE = 2 * TILE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
-  const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63;
   // Wave index in a scalar register: the per-wave tests below (causal skip,
   // masked subtile) are then branches, not per-lane predication.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, li = lane & 31;
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int nqb = (N + BM - 1) / BM;
+  const int nqb_max = (a.max_nq + BM - 1) / BM;
   int b, hq, qb;
-  decode_block(blockIdx.x, a.Hq, a.B, nqb, CAUSAL, b, hq, qb);
-  const int hkv = hq / (a.Hq / a.Hkv);
+  decode_block(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, b, hq, qb);
+  const SeqExtent sq = seq_extent(a, b);
+  const int nq = sq.nq, nk = sq.nk;
   const int q0 = qb * BM;
+  if (q0 >= nq) return;  // uniform over the workgroup: no barrier reached yet
+  const int off = CAUSAL ? nk - nq : 0;
+  const int hkv = hq / (a.Hq / a.Hkv);
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + li;
 
-  const size_t qoff = (size_t)(b * a.Hq + hq) * N;
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + qoff * D;
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + qoff * D;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)(b * a.Hkv + hkv) * N * D;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)(b * a.Hkv + hkv) * N * D;
+  const long long qr = sq.qrow0(b, hq);
+  const long long kr = sq.krow0(b, hkv);
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q) + qr * D;
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout) + qr * D;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + kr * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + kr * D;
 
-  const int nkb = (N + BK - 1) / BK;
-  const int q_last = min(q0 + BM, N) - 1;
-  const int kb_end = CAUSAL ? min(nkb, q_last / BK + 1) : nkb;
+  // Key blocks up to the last key the workgroup's last query sees (none when
+  // that query sees no key: dQ = 0).
+  const int nkb = (nk + BK - 1) / BK;
+  const int kmax = CAUSAL ? min(q0 + BM, nq) - 1 + off : nk - 1;
+  const int kb_end = kmax < 0 ? 0 : min(nkb, kmax / BK + 1);
   BlockDma<D, BK, RS, NW> dma;
   dma.init(wave, lane);
   auto prefetch = [&](int kb) {
     uint8_t* st = smem + (kb & 1) * STAGE;
     const uint16_t* kg = K + (size_t)kb * BK * D;
     const uint16_t* vg = V + (size_t)kb * BK * D;
-    if ((kb + 1) * BK <= N) {
+    if ((kb + 1) * BK <= nk) {
       dma.template issue<true>(st, kg, BK, wave);
       dma.template issue<true>(st + TILE, vg, BK, wave);
     } else {
-      dma.template issue<false>(st, kg, N - kb * BK, wave);
-      dma.template issue<false>(st + TILE, vg, N - kb * BK, wave);
+      dma.template issue<false>(st, kg, nk - kb * BK, wave);
+      dma.template issue<false>(st + TILE, vg, nk - kb * BK, wave);
     }
   };
   if (kb_end > 0) prefetch(0);
@@ -355,11 +408,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
   bf16x8 qf[NF], of[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    qf[f] = (qi < N) ? global_frag<uint16_t>(Q + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
-    of[f] = (qi < N) ? global_frag<uint16_t>(dO + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    qf[f] = (qi < nq) ? global_frag<uint16_t>(Q + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
+    of[f] = (qi < nq) ? global_frag<uint16_t>(dO + (size_t)qi * D + 16 * f + 8 * h) : zero_frag<bf16x8>();
   }
-  const float l2 = (qi < N) ? l2g[qoff + qi] : INFINITY;
-  const float Di = (qi < N) ? a.dsum[qoff + qi] : 0.f;
+  const float l2 = (qi < nq) ? a.l2[qr + qi] : INFINITY;
+  const float Di = (qi < nq) ? a.dsum[qr + qi] : 0.f;
   f32x16 dq_acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) dq_acc[t] = zero16();
@@ -375,8 +428,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int ks0 = kb * BK + 32 * sub;
-      if (ks0 >= N) break;
-      if (CAUSAL && ks0 > qw0 + 31) continue;  // every key follows every query of this wave
+      if (ks0 >= nk) break;
+      if (CAUSAL && ks0 > qw0 + 31 + off) continue;  // every key follows every query of this wave
       const uint8_t* ks = st + sub * 32 * RS;
       const uint8_t* vs = ks + TILE;
       // S^T = K Q^T and dP^T = V dO^T: rows = keys (rho order), column = query li.
@@ -385,14 +438,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
       for (int f = 0; f < NF; ++f) mma(s, *reinterpret_cast<const bf16x8*>(ks + row_off + 32 * f), qf[f]);
 #pragma unroll
       for (int f = 0; f < NF; ++f) mma(dp, *reinterpret_cast<const bf16x8*>(vs + row_off + 32 * f), of[f]);
-      const bool masked = (CAUSAL && ks0 + 31 > qw0) || ks0 + 32 > N;
+      // Masks: key >= nk, or (causal) key > query + off; a query that sees no
+      // key (l2 = -inf) is masked on every key.
+      const bool masked = (CAUSAL && ks0 + 31 > qw0 + off) || ks0 + 32 > nk;
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
         if (masked) {
           const int key = ks0 + rho_row(r, h);
-          if (key >= N || (CAUSAL && key > qi)) pv = 0.f;
+          if (key >= nk || (CAUSAL && key > qi + off)) pv = 0.f;
         }
         ds[r] = pv * (dp[r] - Di);
       }
@@ -408,8 +463,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
     }
   }
 
-  if (qi < N) {
-    uint16_t* dQ = static_cast<uint16_t*>(a.dq) + (qoff + qi) * D;
+  if (qi < nq) {
+    uint16_t* dQ = static_cast<uint16_t*>(a.dq) + (qr + qi) * D;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
@@ -422,27 +477,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdArgs a, const f
   }
 }
 
-
 // The dQ kernel's instances live in their own translation unit (built with
 // MFMA accumulators in VGPRs, which keeps it within two waves per SIMD).
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_prep_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
   // Pairs per workgroup: 4 (two waves per SIMD) while a wave's registers allow
   // it; at d = 256 a wave needs more than half the register file, so 2.
   constexpr int NPKV = D <= 128 ? 4 : 2;
-  const long long rows = (long long)a.B * a.Hq * a.N;
-  float* l2 = a.dsum + bwd_ws_l2_offset(rows) / 4;  // the workspace layout of bwd_ws_bytes
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a,
-                     l2);
-  const int nkb = (a.N + 32 * NPKV - 1) / (32 * NPKV);
+  hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  const int nkb = (a.max_nk + 32 * NPKV - 1) / (32 * NPKV);
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NPKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(128 * NPKV), 0,
-                     stream, a, (const float*)l2);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq_bf16(a, l2, D, CAUSAL ? 1 : 0, stream);
+                     stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace fa

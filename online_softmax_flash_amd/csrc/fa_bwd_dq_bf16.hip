@@ -7,22 +7,22 @@
 namespace fa {
 
 template <int D, bool CAUSAL>
-static hipError_t dq_bf16(const BwdArgs& a, const float* l2, hipStream_t stream) {
+static hipError_t dq_bf16(const BwdKvArgs& a, hipStream_t stream) {
   constexpr int NWQ = 4;
-  const int nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
+  const int nqb = (a.max_nq + 32 * NWQ - 1) / (32 * NWQ);
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NWQ), 0,
-                     stream, a, l2);
+                     stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* l2, int d, int causal, hipStream_t stream) {
+hipError_t launch_bwd_dq_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream) {
   switch (d * 2 + (causal ? 1 : 0)) {
-    case 64 * 2: return dq_bf16<64, false>(a, l2, stream);
-    case 64 * 2 + 1: return dq_bf16<64, true>(a, l2, stream);
-    case 128 * 2: return dq_bf16<128, false>(a, l2, stream);
-    case 128 * 2 + 1: return dq_bf16<128, true>(a, l2, stream);
-    case 256 * 2: return dq_bf16<256, false>(a, l2, stream);
-    case 256 * 2 + 1: return dq_bf16<256, true>(a, l2, stream);
+    case 64 * 2: return dq_bf16<64, false>(a, stream);
+    case 64 * 2 + 1: return dq_bf16<64, true>(a, stream);
+    case 128 * 2: return dq_bf16<128, false>(a, stream);
+    case 128 * 2 + 1: return dq_bf16<128, true>(a, stream);
+    case 256 * 2: return dq_bf16<256, false>(a, stream);
+    case 256 * 2 + 1: return dq_bf16<256, true>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,7 +28,8 @@ struct KvArgs {
   float c;                     // scale * log2(e)
 };
 
-// Arguments of the general backward.
+// Arguments of the bf16 backward (square, rectangular and variable-length
+// problems; see fa_bwd_bf16.hpp).
 struct BwdKvArgs {
   const void* q;
   const void* k;
@@ -40,8 +41,7 @@ struct BwdKvArgs {
   void* dk;
   void* dv;
   float* dsum;      // workspace: D_i = dO_i . O_i, one per query row
-  float* l2;        // workspace: lse_i * log2(e)
-  float* dqa;       // workspace: fp32 dQ accumulator, [rows][d]
+  float* l2;        // workspace: lse_i * log2(e), one per query row
   const int* cu_q;  // variable-length offsets [B+1] (device), or null
   const int* cu_k;
   int B, Hq, Hkv;
@@ -67,24 +67,17 @@ hipError_t fwd_kv_bf16(const KvArgs& a, int d, int causal, hipStream_t stream);
 hipError_t naive_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* s, uint16_t* p,
                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
 
-// Backward: D = rowsum(dO * O) into dsum, then the dK/dV and dQ kernels,
-// all on stream.
-hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                    const void* dout, void* dq, void* dk, void* dv, float* dsum,
-                    int B, int Hq, int Hkv, int N, int d, float scale, float c, int causal, hipStream_t stream);
-// General backward (bf16, d <= 128): D, l2 and a cleared dQ accumulator,
-// then dK, dV and dQ in one pass over the score blocks, then dQ rounded to
-// bf16; all on stream. Square problems are the case Nq = Nk.
-hipError_t bwd_fused_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
+// Backward (bf16): D and l2 into the workspace, then the dK/dV and dQ
+// kernels, all on stream. Square problems are the case Nq = Nk.
+hipError_t bwd_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
 
-// Bytes of the backward workspace for `rows` query rows of head dim d (the
-// layout of BwdKvArgs: D, l2, dQ accumulator, each from a 256-byte boundary).
+// Bytes of the backward workspace for `rows` query rows: D and l2 (fp32
+// each), the second from a 256-byte boundary.
 inline size_t bwd_ws_l2_offset(long long rows) { return ((size_t)rows * 4 + 255) & ~(size_t)255; }
-inline size_t bwd_ws_dqa_offset(long long rows) { return 2 * bwd_ws_l2_offset(rows); }
-inline size_t bwd_ws_bytes(long long rows, int d) {
-  return bwd_ws_dqa_offset(rows) + (((size_t)rows * d * 4 + 255) & ~(size_t)255);
-}
+inline size_t bwd_ws_bytes(long long rows) { return 2 * bwd_ws_l2_offset(rows); }
 
+// Backward, fp32 check mode (square): D = rowsum(dO * O) into dsum, then the
+// dK/dV and dQ kernels, all on stream.
 hipError_t bwd_f32(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv, float* dsum,
                    int B, int Hq, int Hkv, int N, int d, float scale, float c, int causal, hipStream_t stream);

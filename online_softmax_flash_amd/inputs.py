@@ -113,26 +113,31 @@ def make_inputs(
     return AttnInputs(q=q, k=k, v=v, do=do, dtype=dtype, seed=seed, heavy_rows=heavy)
 
 
-def make_kv_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int) -> AttnInputs:
-    """Rectangular problem: Q ``[B, Hq, Nq, d]``, K and V ``[B, Hkv, Nk, d]``,
-    i.i.d. standard normal float32 draws in that order, rounded to bf16."""
+def make_kv_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+                   with_dout: bool = False) -> AttnInputs:
+    """Rectangular problem: Q ``[B, Hq, Nq, d]``, K and V ``[B, Hkv, Nk, d]``
+    (and dO shaped like Q when ``with_dout``), i.i.d. standard normal float32
+    draws in that order, rounded to bf16."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, Nq, d), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
-    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=None, dtype="bf16", seed=seed,
+    do = bf16_round(rng.standard_normal((B, Hq, Nq, d), dtype=np.float32)) if with_dout else None
+    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=do, dtype="bf16", seed=seed,
                       heavy_rows=None)
 
 
-def make_varlen_inputs(Hq: int, Hkv: int, cu_q, cu_k, d: int, seed: int) -> AttnInputs:
+def make_varlen_inputs(Hq: int, Hkv: int, cu_q, cu_k, d: int, seed: int, with_dout: bool = False) -> AttnInputs:
     """Variable-length batch packed along the token axis: Q ``[Hq, Tq, d]``,
-    K and V ``[Hkv, Tk, d]`` with Tq = cu_q[-1], Tk = cu_k[-1]; i.i.d. standard
-    normal float32 draws in that order, rounded to bf16."""
+    K and V ``[Hkv, Tk, d]`` with Tq = cu_q[-1], Tk = cu_k[-1] (and dO shaped
+    like Q when ``with_dout``); i.i.d. standard normal float32 draws in that
+    order, rounded to bf16."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((Hq, int(cu_q[-1]), d), dtype=np.float32)
     k = rng.standard_normal((Hkv, int(cu_k[-1]), d), dtype=np.float32)
     v = rng.standard_normal((Hkv, int(cu_k[-1]), d), dtype=np.float32)
-    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=None, dtype="bf16", seed=seed,
+    do = bf16_round(rng.standard_normal((Hq, int(cu_q[-1]), d), dtype=np.float32)) if with_dout else None
+    return AttnInputs(q=bf16_round(q), k=bf16_round(k), v=bf16_round(v), do=do, dtype="bf16", seed=seed,
                       heavy_rows=None)
 
 

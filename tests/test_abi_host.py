@@ -107,14 +107,17 @@ def test_backward_validation(fn):
 
 def test_workspace_bytes_linear_in_n():
     ws = fa.flash_attn_bwd_workspace_bytes
-    # Per query row: D and lse * log2(e) (fp32 each), then the fp32 dQ
-    # accumulator (d values), each part from a 256-byte boundary.
+    # Per query row: D and lse * log2(e) (fp32 each), the second from a
+    # 256-byte boundary.
     def up(n):
         return (n + 255) // 256 * 256
     R = 2 * 16 * 4096
-    assert ws(2, 16, 16, 4096, 128) == 2 * 4 * R + 4 * R * 128
-    assert ws(1, 1, 1, 1, 64) == 2 * 256 + 256
-    assert ws(1, 2, 1, 1000, 64) == 2 * up(4 * 2000) + up(4 * 2000 * 64)
+    assert ws(2, 16, 16, 4096, 128) == 2 * 4 * R
+    assert ws(1, 1, 1, 1, 64) == 2 * 256
+    assert ws(1, 2, 1, 1000, 64) == 2 * up(4 * 2000)
+    kws = fa.flash_attn_bwd_kv_workspace_bytes
+    assert kws(2 * 16 * 4096, 128) == ws(2, 16, 16, 4096, 128)
+    assert kws(0, 128) == 0 and kws(10, 96) == 0
     assert ws(2, 16, 16, 8192, 128) == 2 * ws(2, 16, 16, 4096, 128)
     assert ws(0, 1, 1, 1, 64) == 0
     assert ws(1, 3, 2, 1, 64) == 0
@@ -216,3 +219,41 @@ def test_noalloc_refuses_partials_beyond_its_scratch():
     assert call((2, 8, 2, 3, 100, 128), 300) == STATUS["FA_ERR_SHAPE"]
     src = open(HEADER).read()
     assert re.search(r"#define FLASH_ATTN_SCRATCH_BYTES \(32u << 20\)", src)
+
+
+def _bwdkv(ptrs=(FAKE,) * 10, shape=(2, 8, 2, 3, 100, 128), scale=0.1, causal=1, ws_bytes=1 << 40):
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return lib.flash_attn_bwd_kv(*p, ctypes.c_size_t(ws_bytes), *shape, ctypes.c_float(scale), causal, None)
+
+
+def test_bwd_kv_and_varlen_reject_bad_arguments():
+    for i in range(10):
+        ptrs = [FAKE] * 10
+        ptrs[i] = 0
+        assert _bwdkv(ptrs) == (STATUS["FA_ERR_WORKSPACE"] if i == 9 else STATUS["FA_ERR_NULL"])
+        ptrs[i] = FAKE + 8
+        assert _bwdkv(ptrs) == STATUS["FA_ERR_ALIGN"]
+    assert _bwdkv(shape=(2, 8, 3, 3, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _bwdkv(shape=(2, 8, 2, 0, 100, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _bwdkv(shape=(2, 8, 2, 3, 0, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert _bwdkv(shape=(2, 8, 2, 3, 100, 32)) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert _bwdkv(causal=2) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert _bwdkv(scale=math.nan) == STATUS["FA_ERR_SCALE"]
+    need = fa.flash_attn_bwd_kv_workspace_bytes(2 * 8 * 3, 128)
+    assert need > 0
+    assert _bwdkv(ws_bytes=need - 1) == STATUS["FA_ERR_WORKSPACE"]
+    lib = fa.load_library()
+    p = [ctypes.c_void_p(FAKE)] * 9
+
+    def varlen(cu=(FAKE, FAKE), shape=(2, 8, 2, 50, 60, 30, 40, 128), ws_bytes=1 << 40):
+        c = [ctypes.c_void_p(x) if x else None for x in cu]
+        return lib.flash_attn_bwd_varlen(*p, *c, ctypes.c_void_p(FAKE), ctypes.c_size_t(ws_bytes), *shape,
+                                         ctypes.c_float(0.1), 1, None)
+
+    assert varlen(cu=(0, FAKE)) == STATUS["FA_ERR_NULL"]
+    assert varlen(cu=(FAKE, 0)) == STATUS["FA_ERR_NULL"]
+    assert varlen(shape=(0, 8, 2, 50, 60, 30, 40, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert varlen(shape=(2, 8, 2, 50, 60, 0, 40, 128)) == STATUS["FA_ERR_SHAPE"]
+    assert varlen(shape=(2, 8, 2, 50, 60, 30, 40, 80)) == STATUS["FA_ERR_UNSUPPORTED"]
+    assert varlen(ws_bytes=fa.flash_attn_bwd_kv_workspace_bytes(8 * 50, 128) - 1) == STATUS["FA_ERR_WORKSPACE"]
