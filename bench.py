@@ -137,6 +137,27 @@ def clock_ramp(fn, stream, seconds):
     return {"seconds": round(time.perf_counter() - t0, 3), "launches": n}
 
 
+def time_backward(fn, stream, flops, launches):
+    """Backward pass timed like the forward steps: one untimed launch and
+    0.3 s of untimed back-to-back launches (the clock is already up from the
+    forward), then `launches` timed back to back with HIP events on the launch
+    stream, and the median of 5 trials of 3 launches beside it."""
+    import torch
+    fn()
+    clock_ramp(fn, stream, 0.3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "tflops": round(tf, 3), "steps": launches, "credited_flops": flops,
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+            "timing": timing_trials(fn, stream, trials=5, per=3)}
+
+
 def timing_trials(fn, stream, trials=20, per=10):
     """Per-launch time over `trials` runs of `per` back-to-back launches
     (HIP events on the launch stream): median and minimum, in ms."""
@@ -329,19 +350,8 @@ def main():
                          dtype=torch.uint8, device=dev)
         bwd = fa.flash_attn_bwd if w.dtype == "bf16" else fa.flash_attn_bwd_f32
         try:
-            bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale, causal)
-            torch.cuda.synchronize()
-            nb = max(3, args.steps // 5)
-            ev0.record(stream)
-            for _ in range(nb):
-                bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale, causal)
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            bms = ev0.elapsed_time(ev1) / nb
-            btf = w.bwd_flops(causal) / (bms * 1e-3) / 1e12
-            result["backward"] = {"ms": round(bms, 5), "tflops": round(btf, 3), "steps": nb,
-                                  "credited_flops": w.bwd_flops(causal),
-                                  "pct_of_peak": round(100.0 * btf / PEAK_BF16_TFLOPS, 2)}
+            result["backward"] = time_backward(lambda: bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.scale, causal),
+                                               stream, w.bwd_flops(causal), max(10, args.steps // 2))
         except fa.FlashAttnError as e:
             result["backward"] = {"error": str(e)}
 
@@ -386,13 +396,13 @@ def bench_kv(args, w):
     lens = w.lengths()
     if w.lengths_seed:
         cu = np.concatenate([[0], np.cumsum([nq for nq, _ in lens])]).astype(np.int64)
-        inp = make_varlen_inputs(w.Hq, w.Hkv, cu, cu, w.d, w.seed)
+        inp = make_varlen_inputs(w.Hq, w.Hkv, cu, cu, w.d, w.seed, with_dout=not args.no_backward)
         cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
         max_q = int(max(nq for nq, _ in lens))
         max_k = int(max(nk for _, nk in lens))
         rows = w.Hq * int(cu[-1])
     else:
-        inp = make_kv_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+        inp = make_kv_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed, with_dout=not args.no_backward)
         max_q, max_k = w.Nq, w.Nk
         rows = w.B * w.Hq * w.Nq
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (inp.q, inp.k, inp.v))
@@ -455,6 +465,23 @@ def bench_kv(args, w):
         "wall_s_timed_region": round(wall_s, 4),
         "clock_ramp": ramp,
     }
+    if not args.no_backward and splits == 1:
+        # The general backward over the same problem (o and lse from the
+        # forward above): one step = D and l2, the dK/dV and the dQ kernels.
+        do = torch.from_numpy(inp.do).to(torch.bfloat16).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wsb = torch.empty(max(fa.flash_attn_bwd_kv_workspace_bytes(rows, w.d), 256), dtype=torch.uint8, device=dev)
+
+        def bstep():
+            if w.lengths_seed:
+                fa.flash_attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_t, cu_t, max_q, max_k, wsb, w.scale,
+                                         w.causal)
+            else:
+                fa.flash_attn_bwd_kv(q, k, v, o, lse, do, dq, dk, dv, wsb, w.scale, w.causal)
+
+        result["backward"] = time_backward(bstep, stream, 2.5 * flops, max(10, args.steps // 2))
+        result["backward"]["kernels"] = "bwd_prep_bf16_kernel, bwd_dkdv_bf16_kernel, bwd_dq_bf16_kernel"
+
     if not args.no_cpu_baseline:
         import oracle
         G = w.Hq // w.Hkv

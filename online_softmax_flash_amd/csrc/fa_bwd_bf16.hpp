@@ -120,6 +120,27 @@ __device__ __forceinline__ SeqExtent seq_extent(const BwdKvArgs& a, int b) {
   return e;
 }
 
+// Work item of workgroup wg: (sequence b, head h, block kb) out of HB = H*B
+// (sequence, head) pairs times nb blocks, block-major (all pairs' block 0
+// first). Uniform batches use decode_block's order (each XCD a contiguous
+// range of pairs). Variable-length batches take pair wg % HB, so that with
+// round-robin dispatch over the 8 XCDs every XCD receives heads of every
+// sequence: a long sequence's work is spread over the chip instead of
+// landing on the XCD its pairs would occupy (every block of a pair still
+// runs on one XCD).
+__device__ __forceinline__ void decode_item(int wg, int H, int B, int nb, bool reverse, bool varlen, int& b, int& h,
+                                            int& kb) {
+  if (!varlen) {
+    decode_block(wg, H, B, nb, reverse, b, h, kb);
+    return;
+  }
+  const int HB = H * B;
+  const int level = wg / HB, wp = wg % HB;
+  b = wp / H;
+  h = wp % H;
+  kb = reverse ? (nb - 1 - level) : level;
+}
+
 // D = dO . O and l2 = lse * log2(e) per query row; one row per D/8 threads.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdKvArgs a) {
@@ -177,7 +198,7 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
   const int G = a.Hq / a.Hkv;
   const int nkb_max = (a.max_nk + BKV - 1) / BKV;
   int b, hkv, kb;
-  decode_block(blockIdx.x, a.Hkv, a.B, nkb_max, false, b, hkv, kb);  // key block 0 has the most work
+  decode_item(blockIdx.x, a.Hkv, a.B, nkb_max, false, a.cu_q != nullptr, b, hkv, kb);  // key block 0 has the most work
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
   const int k0 = kb * BKV;
@@ -367,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
   const int g16 = lane >> 4, i16 = lane & 15;
   const int nqb_max = (a.max_nq + BM - 1) / BM;
   int b, hq, qb;
-  decode_block(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, b, hq, qb);
+  decode_item(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
   const int q0 = qb * BM;
