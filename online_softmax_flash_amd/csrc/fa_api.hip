@@ -157,13 +157,15 @@ int bwd_kv_common(const void* q, const void* k, const void* v, const void* o, co
 // Split count for the general forward: one unless the (batch, K/V head, row
 // block) workgroups are too few to fill the chip; then enough splits for about
 // four workgroups per compute unit (eight for one-wave decoding workgroups,
-// whose work is streaming K and V), each split at least 256 keys.
-int kv_splits_auto(int B, int Hq, int Hkv, int max_nq, int max_nk) {
+// whose work is streaming K and V), each split at least 256 keys. At d = 256
+// one four-wave workgroup fills a compute unit's LDS: a grid of 256 of them
+// already fills the chip, and the four-wave target halves.
+int kv_splits_auto(int B, int Hq, int Hkv, int max_nq, int max_nk, int d) {
   const long long G = Hq / Hkv;
   const long long rows = (long long)max_nq * G;
   const long long bm = rows <= 32 ? 32 : 128;
   const long long wgs = (long long)B * Hkv * ((rows + bm - 1) / bm);
-  const long long target = (rows <= 32 ? 8 : 4) * 256;
+  const long long target = (rows <= 32 ? 8 : (d == 256 ? 2 : 4)) * 256;
   if (wgs >= target / 2 || max_nk <= 512) return 1;
   long long s = (target + wgs - 1) / wgs;
   s = s < (max_nk + 255) / 256 ? s : (max_nk + 255) / 256;
@@ -221,11 +223,14 @@ int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (rows * d > ((long long)1 << 40) || krows * d > ((long long)1 << 40)) return FA_ERR_SHAPE;
   const long long G = Hq / Hkv;
   const long long nrb = ((long long)max_nq * G + 31) / 32;
-  if ((long long)max_nq * G > 0x7fffffffLL || nrb * 256 > 0x7fffffffLL || Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;
+  const long long hb = (long long)Hkv * B;
+  if ((long long)max_nq * G > 0x7fffffffLL || nrb * 256 > 0x7fffffffLL || hb > 0x7fffffffLL) return FA_ERR_SHAPE;
   st = check_scale(scale);
   if (st != FA_OK) return st;
-  int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk) : num_splits;
+  int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk, d) : num_splits;
   if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
+  // Workgroups (32-row blocks at the smallest) within the 65536 x 65535 grid.
+  if (nrb * splits * hb > 65536LL * 65535) return FA_ERR_SHAPE;
   if (use_scratch && splits > 1) {
     if (num_splits == 0)
       while (splits > 1 && kv_workspace(rows, d, splits) > (size_t)FLASH_ATTN_SCRATCH_BYTES) --splits;
@@ -329,7 +334,7 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
 int flash_attn_fwd_kv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Nq <= 0 || Nk <= 0) return 0;
   if (d != 64 && d != 128 && d != 256) return 0;
-  return kv_splits_auto(B, Hq, Hkv, Nq, Nk);
+  return kv_splits_auto(B, Hq, Hkv, Nq, Nk, d);
 }
 
 size_t flash_attn_fwd_kv_workspace_bytes(long long rows, int d, int num_splits) {

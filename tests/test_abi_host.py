@@ -150,6 +150,9 @@ def test_kv_rejects_bad_arguments():
     assert _kv(scale=math.inf) == STATUS["FA_ERR_SCALE"]
     assert _kv(splits=-1) == STATUS["FA_ERR_SHAPE"]
     assert _kv(splits=257) == STATUS["FA_ERR_SHAPE"]
+    # More workgroups than a 65536 x 65535 grid holds (65536 sequences x 1024
+    # K/V heads x 256 splits).
+    assert _kv(shape=(1 << 16, 1024, 1024, 1, 64, 128), splits=256) == STATUS["FA_ERR_SHAPE"]
     # Split keys need the partials' workspace, of at least the stated size, aligned.
     rows = 2 * 8 * 3
     need = fa.flash_attn_fwd_kv_workspace_bytes(rows, 128, 4)
@@ -178,6 +181,10 @@ def test_kv_workspace_and_split_choice():
     # A long prefill fills the chip without splitting; short key ranges are never split.
     assert ns(1, 32, 32, 8192, 8192, 128) == 1
     assert ns(1, 8, 8, 1, 300, 128) == 1
+    # 256 four-wave workgroups: half the chip's slots at d = 128 (split), all
+    # of them at d = 256, where one fills a compute unit's LDS (no split).
+    assert ns(1, 16, 16, 2048, 8192, 128) >= 2
+    assert ns(1, 16, 16, 2048, 8192, 256) == 1
     assert ns(1, 8, 3, 1, 300, 128) == 0
 
 

@@ -178,3 +178,17 @@ def test_kv_decode_very_long_cache():
         o, lse = fa.attention_forward_kv(q, k, v, 1.0 / math.sqrt(d), True, num_splits=splits)
         torch.cuda.synchronize()
         check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, f"very long cache splits={splits}")
+
+
+def test_kv_two_grid_rows():
+    """A grid of more than 65536 workgroups, laid out over two grid rows: 64
+    sequences x 8 K/V heads x 256 splits of a 1000-key cache (split 16 on
+    hold no key), every row against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d = 64, 8, 8, 1, 1000, 128
+    announce(f"kv two grid rows shape={(B, Hq, Hkv, Nq, Nk, d)} splits=256 seed=36")
+    inp = make_kv_inputs(B, Hq, Hkv, Nq, Nk, d, seed=36)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, inp.k, inp.v, 1.0 / math.sqrt(d), True)
+    o, lse = fa.attention_forward_kv(q, k, v, 1.0 / math.sqrt(d), True, num_splits=256)
+    torch.cuda.synchronize()
+    check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, "two grid rows")
