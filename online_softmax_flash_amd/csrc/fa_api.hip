@@ -229,8 +229,11 @@ int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (st != FA_OK) return st;
   int splits = num_splits == 0 ? kv_splits_auto(B, Hq, Hkv, max_nq, max_nk, d) : num_splits;
   if (splits < 1 || splits > 256) return FA_ERR_SHAPE;
-  // Workgroups (32-row blocks at the smallest) within the 65536 x 65535 grid.
-  if (nrb * splits * hb > 65536LL * 65535) return FA_ERR_SHAPE;
+  // Workgroups (32-row blocks at the smallest) within the 65536 x 65535 grid;
+  // variable-length batches of up to 256 sequences take the compact grid.
+  const bool compact = cu_q != nullptr && B <= 256;
+  const long long items = compact ? ((long long)Nq * G + 31) / 32 + B : nrb * B;
+  if (items * splits * Hkv > 65536LL * 65535) return FA_ERR_SHAPE;
   if (use_scratch && splits > 1) {
     if (num_splits == 0)
       while (splits > 1 && kv_workspace(rows, d, splits) > (size_t)FLASH_ATTN_SCRATCH_BYTES) --splits;
@@ -262,6 +265,7 @@ int kv_common(const void* q, const void* k, const void* v, void* o, float* lse, 
   a.max_nq = max_nq;
   a.max_nk = max_nk;
   a.num_splits = splits;
+  a.compact = compact ? 1 : 0;
   a.split_keys = (((max_nk + splits - 1) / splits) + 63) / 64 * 64;
   a.rows = rows;
   a.c = scale * kLog2e;

@@ -55,26 +55,69 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   // first; with one split and pairs a multiple of 8, each XCD receives a
   // contiguous range of (batch, K/V head) pairs, whose K and V then stay in
   // its L2. A variable-length batch goes pair by pair, heaviest row block
-  // first within each: level by level it ran 1.6x slower on a batch of 16
-  // sequences of 99-3885 tokens, where most row blocks of the top levels lie
-  // beyond the shorter sequences and are dispatched only to exit.
+  // first within each, over the row blocks its sequences actually have
+  // (compact grid): a grid of max_seqlen row blocks for every sequence spent
+  // most of its workgroups on row blocks past the shorter sequences, each
+  // dispatched only to read the offsets and exit.
   const long long wg = (long long)blockIdx.y * gridDim.x + blockIdx.x;
   const int HB = a.Hkv * a.B;
-  const int nrb = (int)(((long long)a.max_nq * G + BM - 1) / BM);
   const int split = (int)(wg % a.num_splits);
   const long long item = wg / a.num_splits;
-  if (item >= (long long)nrb * HB) return;  // grid padding; uniform over the workgroup
-  int level, pair;
-  if (a.cu_q != nullptr) {
-    pair = (int)(item / nrb);
-    level = (int)(item % nrb);
+  int b, hkv, rb;
+  if (a.compact) {
+    // Sequence s has cnt_s = ceil(n_s * G / BM) row blocks (n_s clamped as
+    // below); items run over s, then K/V head, then row block. Every wave
+    // finds its item's sequence by a prefix sum over chunks of 64 sequences.
+    long long k = item;
+    int seq = -1, loc = 0, cnt_s = 1;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int sb = c0 + lane;
+      int cnt = 0;
+      if (sb < a.B) {
+        const int s0 = min(max(a.cu_q[sb], 0), a.Nq);
+        const int n = min(min(max(a.cu_q[sb + 1], s0), a.Nq) - s0, a.max_nq);
+        cnt = (int)(((long long)n * G + BM - 1) / BM);
+      }
+      long long incl = (long long)cnt * a.Hkv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const long long excl = incl - (long long)cnt * a.Hkv;
+      const unsigned long long hit = __ballot(k >= excl && k < incl);
+      if (hit != 0) {  // uniform: k is the same in every lane
+        const int l = __ffsll((long long)hit) - 1;
+        seq = c0 + l;
+        loc = (int)(k - __shfl(excl, l));
+        cnt_s = __shfl(cnt, l);
+        break;
+      }
+      k -= __shfl(incl, 63);
+    }
+    if (seq < 0) return;  // grid padding; uniform over the workgroup
+    b = __builtin_amdgcn_readfirstlane(seq);
+    loc = __builtin_amdgcn_readfirstlane(loc);
+    cnt_s = __builtin_amdgcn_readfirstlane(cnt_s);
+    hkv = loc / cnt_s;
+    const int level = loc % cnt_s;
+    rb = CAUSAL ? cnt_s - 1 - level : level;
   } else {
-    level = (int)(item / HB);
-    const int wp = (int)(item % HB);
-    pair = (a.num_splits == 1 && HB % 8 == 0) ? (wp % 8) * (HB / 8) + wp / 8 : wp;
+    const int nrb = (int)(((long long)a.max_nq * G + BM - 1) / BM);
+    if (item >= (long long)nrb * HB) return;  // grid padding; uniform over the workgroup
+    int level, pair;
+    if (a.cu_q != nullptr) {
+      pair = (int)(item / nrb);
+      level = (int)(item % nrb);
+    } else {
+      level = (int)(item / HB);
+      const int wp = (int)(item % HB);
+      pair = (a.num_splits == 1 && HB % 8 == 0) ? (wp % 8) * (HB / 8) + wp / 8 : wp;
+    }
+    b = pair / a.Hkv;
+    hkv = pair % a.Hkv;
+    rb = CAUSAL ? nrb - 1 - level : level;
   }
-  const int b = pair / a.Hkv, hkv = pair % a.Hkv;
-  const int rb = CAUSAL ? nrb - 1 - level : level;
 
   // Sequence b: query rows qs .. qs+nq-1, key rows ks .. ks+nk-1 of each head.
   int qs = 0, nq = a.Nq, ks = 0, nk = a.Nk;
@@ -411,10 +454,13 @@ hipError_t launch_fwd_kv_bf16(const KvArgs& a, hipStream_t stream) {
   // LDS per workgroup, so twice as many workgroups stream K and V per CU.
   constexpr int BN = NW == 1 ? 32 : 64;
   const int G = a.Hq / a.Hkv;
-  const long long nrb = ((long long)a.max_nq * G + BM - 1) / BM;
+  // Items: row blocks of every (sequence, K/V head); a compact variable-length
+  // grid bounds them by the total rows: sum_s ceil(n_s G / BM) <= Tq G / BM + B.
+  const long long nrb = a.compact ? ((long long)a.Nq * G + BM - 1) / BM + a.B
+                                  : ((long long)a.max_nq * G + BM - 1) / BM * a.B;
   // Linear workgroup ids laid out x-major; 65536 (a multiple of 8) per grid
   // row keeps the XCD of a workgroup that of its linear id.
-  const long long total = nrb * a.num_splits * a.Hkv * a.B;
+  const long long total = nrb * a.num_splits * a.Hkv;
   const long long gx = total < 65536 ? total : 65536;
   const long long gy = (total + gx - 1) / gx;
   hipLaunchKernelGGL((fwd_kv_bf16_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)gx, (unsigned)gy), dim3(64 * NW), 0,

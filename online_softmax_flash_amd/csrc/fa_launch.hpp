@@ -24,6 +24,7 @@ struct KvArgs {
   int Nq, Nk;          // uniform: lengths; variable length: totals Tq, Tk
   int max_nq, max_nk;  // largest sequence lengths (grid sizing)
   int num_splits, split_keys;  // keys per split: a multiple of 64
+  int compact;                 // variable length: grid of the sequences' row blocks only (B <= 256)
   long long rows;              // number of (batch, head, query) rows
   float c;                     // scale * log2(e)
 };
