@@ -502,16 +502,32 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
 // MFMA accumulators in VGPRs, which keeps it within two waves per SIMD).
 hipError_t launch_bwd_dq_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_prep_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
-  // Pairs per workgroup: 4 (two waves per SIMD) while a wave's registers allow
-  // it; at d = 256 a wave needs more than half the register file, so 2.
-  constexpr int NPKV = D <= 128 ? 4 : 2;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+template <int D, int NPKV, bool CAUSAL>
+void launch_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
   const int nkb = (a.max_nk + 32 * NPKV - 1) / (32 * NPKV);
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NPKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(128 * NPKV), 0,
                      stream, a);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_prep_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  // Pairs per workgroup: 4 (two waves per SIMD) while a wave's registers allow
+  // it; at d = 256 a wave needs more than half the register file, so 2. At
+  // d = 128 with the causal mask, 6 pairs (three waves per SIMD, 192 keys per
+  // workgroup; the compiler keeps the wave within 168 registers with 2
+  // spilled) when that still gives every compute unit four workgroups or more
+  // to run one after another: 2-4% faster at 8192 tokens, slower on grids of
+  // one or two rounds, where the larger workgroups leave the last round short.
+  if constexpr (D == 128 && CAUSAL) {
+    const long long wgs6 = (long long)((a.max_nk + 191) / 192) * a.Hkv * a.B;
+    if (a.cu_q == nullptr && wgs6 >= 4LL * device_cu_count()) {
+      launch_dkdv_bf16<D, 6, CAUSAL>(a, stream);
+      return hipGetLastError();
+    }
+  }
+  launch_dkdv_bf16<D, (D <= 128 ? 4 : 2), CAUSAL>(a, stream);
   return hipGetLastError();
 }
 

@@ -99,6 +99,37 @@ def test_bwd_full_size(name, causal, groups):
         assert err <= tol, f"{name} {what}: {err:.3e} > {tol:.3e}"
 
 
+def test_bwd_long_8k_shape_full_size():
+    """The headline shape (B=1, H=32, N=8192, d=128, causal, seed 2), whose grid
+    of 1376 six-pair dK/dV workgroups takes the larger-workgroup path, without
+    the workload's ×8 query rows: two whole heads against the oracle and the
+    invariants on every head. (With the ×8 rows, dK of the few keys those rows
+    attend to departs by up to 0.08 from the oracle: D = dO·O uses the stored
+    bf16 O, whose rounding meets the cancellation in dP − D of a peaked row and
+    the ×8 query in dK = scale·dSᵀQ.)"""
+    w = WORKLOADS["long_8k"]
+    announce(f"bwd full long_8k shape without heavy rows ({w.B},{w.Hq},{w.Hkv},{w.N},{w.d}) seed={w.seed}")
+    inp = make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, seed=w.seed, dtype=w.dtype, heavy_frac=0.0, with_dout=True)
+    dq, dk, dv = run_fwd_bwd(inp, w.scale, True)
+    dq_h, dk_h, dv_h = (from_dev(x) for x in (dq, dk, dv))
+    for x in (dq_h, dk_h, dv_h):
+        assert np.all(np.isfinite(x))
+    rng = np.random.default_rng(2100 + w.seed)
+    for h in rng.choice(w.Hq, size=2, replace=False):
+        h = int(h)
+        rq, rk, rv = oracle.attn_bwd_group(inp.q[0, h:h + 1], inp.k[0, h], inp.v[0, h], inp.do[0, h:h + 1], w.scale,
+                                           True)
+        assert_close(dq_h[0, h:h + 1], rq, "bf16", f"long_8k dQ h={h}")
+        assert_close(dk_h[0, h], rk, "bf16", f"long_8k dK h={h}")
+        assert_close(dv_h[0, h], rv, "bf16", f"long_8k dV h={h}")
+    do = inp.do.astype(np.float64)
+    for arr, expect, what in ((dk_h, np.zeros((w.B, w.Hkv, w.d)), "sum dK"), (dv_h, do.sum(axis=2), "sum dV")):
+        got = arr.sum(axis=2)
+        tol = 8.0 * math.sqrt(w.N) * 2.0 ** -9 * float(np.sqrt(np.mean(arr ** 2))) + 1e-3
+        err = float(np.max(np.abs(got - expect)))
+        assert err <= tol, f"long_8k {what}: {err:.3e} > {tol:.3e}"
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_bwd_repeatable(d):
     """No atomics: two runs give identical bits."""
