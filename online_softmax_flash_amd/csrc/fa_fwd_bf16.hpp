@@ -250,7 +250,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   };
   struct Item {
     int b, hq, q0, kb_end, kb_full;
-    size_t kv;  // element offset of the item's K/V head (computed once per item, not per block)
   };
   auto make_item = [&](int it) {
     Item x;
@@ -262,7 +261,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     // Blocks [0, kb_full) need no mask for any query of the workgroup: every
     // key is < N and (causal) <= the first query q0.
     x.kb_full = CAUSAL ? min((x.q0 + 1) / BN, N / BN) : N / BN;
-    x.kv = (size_t)(x.b * a.Hkv + x.hq / (a.Hq / a.Hkv)) * N * D;
     return x;
   };
 
@@ -273,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   // Block kb of item x into LDS stage st (0 or 1).
   auto copy_block = [&](const Item& x, int kb, int st_idx) {
     uint8_t* st = smem + st_idx * STAGE;
-    const size_t off = x.kv + (size_t)kb * BN * D;
+    const size_t off = ((size_t)(x.b * a.Hkv + x.hq / (a.Hq / a.Hkv)) * N + (size_t)kb * BN) * D;
     const uint16_t* kg = static_cast<const uint16_t*>(a.k) + off;
     const uint16_t* vg = static_cast<const uint16_t*>(a.v) + off;
     if (kb < nfull_rows) {
