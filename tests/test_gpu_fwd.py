@@ -142,6 +142,9 @@ MULTI_ROUND = [
     (2, 64, 16, 1000, 128),
     (2, 64, 64, 1024, 128),
     (1, 128, 8, 777, 64),
+    # d = 64 on a long sequence takes 16-wave workgroups (512 rows): 5 query
+    # blocks x 128 heads = 640 items, three rounds; ragged N; GQA.
+    (1, 128, 16, 2100, 64),
 ]
 
 
