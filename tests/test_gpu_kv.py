@@ -194,21 +194,26 @@ def test_kv_two_grid_rows():
     check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, "two grid rows")
 
 
-@pytest.mark.parametrize("n_seq", [64, 256, 300], ids=["64-compact", "256-compact", "300-full-grid"])
+MANY = [(64, 4, 2), (64, 16, 8), (256, 4, 2), (300, 4, 2)]
+
+
+@pytest.mark.parametrize("n_seq,Hq,Hkv", MANY, ids=["64-compact", "64-compact-xcd-heads", "256-compact", "300-full-grid"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_many_sequences(n_seq, causal):
+def test_varlen_many_sequences(n_seq, Hq, Hkv, causal):
     """Many short sequences (0-150 queries, 0-200 keys each, seeded): the
     compact grid of the sequences' row blocks, found by a prefix sum over
     chunks of 64 sequences (64: one chunk; 256: four, the largest batch that
-    takes it) and the full grid of max_seqlen row blocks per sequence (300
-    sequences); every row against the oracle."""
+    takes it; 8 K/V heads: the order that gives each XCD its own heads) and
+    the full grid of max_seqlen row blocks per sequence (300 sequences);
+    every row against the oracle."""
     rng = np.random.default_rng(1000 + n_seq)
     lq = rng.integers(0, 151, size=n_seq)
     lk = rng.integers(0, 201, size=n_seq)
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
     cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
-    Hq, Hkv, d = 4, 2, 64
-    announce(f"varlen many sequences n_seq={n_seq} Tq={int(cu_q[-1])} Tk={int(cu_k[-1])} causal={causal} seed=37")
+    d = 64
+    announce(f"varlen many sequences n_seq={n_seq} Hq={Hq} Hkv={Hkv} Tq={int(cu_q[-1])} Tk={int(cu_k[-1])} "
+             f"causal={causal} seed=37")
     inp = make_varlen_inputs(Hq, Hkv, cu_q, cu_k, d, seed=37)
     q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
     cq = torch.tensor(cu_q, dtype=torch.int32, device="cuda")
