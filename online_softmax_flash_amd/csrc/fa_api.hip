@@ -83,6 +83,7 @@ fa::BwdKvArgs bwd_args(const void* q, const void* k, const void* v, const void* 
   a.Nk = Nk;
   a.max_nq = max_nq;
   a.max_nk = max_nk;
+  a.compact = (cu_q != nullptr && B <= 256) ? 1 : 0;
   a.rows = rows;
   a.c = scale * kLog2e;
   a.scale = scale;

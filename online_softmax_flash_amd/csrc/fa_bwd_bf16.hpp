@@ -198,7 +198,17 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
   const int G = a.Hq / a.Hkv;
   const int nkb_max = (a.max_nk + BKV - 1) / BKV;
   int b, hkv, kb;
-  decode_item(blockIdx.x, a.Hkv, a.B, nkb_max, false, a.cu_q != nullptr, b, hkv, kb);  // key block 0 has the most work
+  if (a.compact) {
+    // Variable length: the sequences' key blocks only, key block 0 (the most
+    // work) first; XCD x takes K/V heads x, x + 8, ... when they divide by 8.
+    const bool by_xcd = a.Hkv % 8 == 0;
+    int j, cnt;
+    if (!compact_item(blockIdx.x, a.cu_k, a.B, a.Nk, a.max_nk, 1, BKV, a.Hkv, by_xcd, lane, b, j, kb, cnt))
+      return;  // grid padding; uniform over the workgroup
+    hkv = by_xcd ? (int)(blockIdx.x % 8) + 8 * j : j;
+  } else {
+    decode_item(blockIdx.x, a.Hkv, a.B, nkb_max, false, a.cu_q != nullptr, b, hkv, kb);  // key block 0 has the most work
+  }
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
   const int k0 = kb * BKV;
@@ -388,7 +398,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
   const int g16 = lane >> 4, i16 = lane & 15;
   const int nqb_max = (a.max_nq + BM - 1) / BM;
   int b, hq, qb;
-  decode_item(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
+  if (a.compact) {
+    // Variable length: the sequences' query blocks only, the last (causal:
+    // the most work) first; with K/V heads a multiple of 8, XCD x takes the
+    // query heads of K/V heads x, x + 8, ..., whose K and V it then reads.
+    const int G = a.Hq / a.Hkv;
+    const bool by_xcd = a.Hkv % 8 == 0;
+    int j, level, cnt;
+    if (!compact_item(blockIdx.x, a.cu_q, a.B, a.Nq, a.max_nq, 1, BM, a.Hq, by_xcd, lane, b, j, level, cnt))
+      return;  // grid padding; uniform over the workgroup
+    hq = by_xcd ? ((int)(blockIdx.x % 8) + 8 * (j / G)) * G + j % G : j;
+    qb = CAUSAL ? cnt - 1 - level : level;
+  } else {
+    decode_item(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
+  }
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
   const int q0 = qb * BM;
@@ -504,8 +527,11 @@ hipError_t launch_bwd_dq_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t
 
 template <int D, int NPKV, bool CAUSAL>
 void launch_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
-  const int nkb = (a.max_nk + 32 * NPKV - 1) / (32 * NPKV);
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NPKV, CAUSAL>), dim3((unsigned)(nkb * a.Hkv * a.B)), dim3(128 * NPKV), 0,
+  constexpr int BKV = 32 * NPKV;
+  // Compact variable-length grid: sum_s ceil(nk_s / BKV) <= Tk / BKV + B.
+  const long long items = a.compact ? ((long long)a.Nk + BKV - 1) / BKV + a.B
+                                    : (long long)((a.max_nk + BKV - 1) / BKV) * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, NPKV, CAUSAL>), dim3((unsigned)(items * a.Hkv)), dim3(128 * NPKV), 0,
                      stream, a);
 }
 

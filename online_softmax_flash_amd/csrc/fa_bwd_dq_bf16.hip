@@ -8,10 +8,12 @@ namespace fa {
 
 template <int D, bool CAUSAL>
 static hipError_t dq_bf16(const BwdKvArgs& a, hipStream_t stream) {
-  constexpr int NWQ = 4;
-  const int nqb = (a.max_nq + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(nqb * a.Hq * a.B)), dim3(64 * NWQ), 0,
-                     stream, a);
+  constexpr int NWQ = 4, BM = 32 * NWQ;
+  // Compact variable-length grid: sum_s ceil(nq_s / BM) <= Tq / BM + B.
+  const long long items = a.compact ? ((long long)a.Nq + BM - 1) / BM + a.B
+                                    : (long long)((a.max_nq + BM - 1) / BM) * a.B;
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NWQ, CAUSAL>), dim3((unsigned)(items * a.Hq)), dim3(64 * NWQ), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -234,4 +234,54 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
 }
 
+// Item `item` of a compact grid over a variable-length batch: sequence s
+// (rows cu[s] .. cu[s+1], clamped into [0, total] and to max_len rows, as the
+// kernels clamp them) has cnt_s = ceil(len_s * mult / blk) blocks; the items
+// run over sequences, then over block levels, then over the heads of the list
+// (so that a sequence's heaviest blocks of every head come first). With
+// xcd_heads (H a multiple of 8 and one item per workgroup in dispatch order),
+// the items of XCD x = item % 8 are those of heads x, x + 8, ... only; the
+// returned head index j then counts those heads (head = x + 8 * j). Every lane
+// of the wave finds the sequence by a prefix sum over chunks of 64 sequences
+// and returns the same, wave-uniform, values. False: grid padding.
+__device__ __forceinline__ bool compact_item(long long item, const int* cu, int B, int total, int max_len, int mult,
+                                             int blk, int H, bool xcd_heads, int lane, int& seq, int& j, int& level,
+                                             int& cnt_seq) {
+  const int hper = xcd_heads ? H / 8 : H;
+  long long k = xcd_heads ? item / 8 : item;
+  int s_found = -1, loc = 0, cnt_found = 1;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int sb = c0 + lane;
+    int cnt = 0;
+    if (sb < B) {
+      const int s0 = min(max(cu[sb], 0), total);
+      const int n = min(min(max(cu[sb + 1], s0), total) - s0, max_len);
+      cnt = (int)(((long long)n * mult + blk - 1) / blk);
+    }
+    long long incl = (long long)cnt * hper;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const long long excl = incl - (long long)cnt * hper;
+    const unsigned long long hit = __ballot(k >= excl && k < incl);
+    if (hit != 0) {  // uniform: k is the same in every lane
+      const int l = __ffsll((long long)hit) - 1;
+      s_found = c0 + l;
+      loc = (int)(k - __shfl(excl, l));
+      cnt_found = __shfl(cnt, l);
+      break;
+    }
+    k -= __shfl(incl, 63);
+  }
+  if (s_found < 0) return false;
+  seq = __builtin_amdgcn_readfirstlane(s_found);
+  loc = __builtin_amdgcn_readfirstlane(loc);
+  cnt_seq = __builtin_amdgcn_readfirstlane(cnt_found);
+  level = loc / hper;
+  j = loc % hper;
+  return true;
+}
+
 }  // namespace fa

@@ -65,48 +65,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   const long long item = wg / a.num_splits;
   int b, hkv, rb;
   if (a.compact) {
-    // Sequence s has cnt_s = ceil(n_s * G / BM) row blocks (n_s clamped as
-    // below); items run over s, then K/V head, then row block. Every wave
-    // finds its item's sequence by a prefix sum over chunks of 64 sequences.
-    // With one split and K/V heads a multiple of 8, the items of XCD x
-    // (item % 8, the dispatch order) are those of heads x, x + 8, ... of
-    // every sequence, so each head's K and V are read through one L2
-    // (varlen_mix 285 -> 278 us); every XCD still gets an equal share.
+    // Sequence s has ceil(n_s * G / BM) row blocks; items run over sequences,
+    // then K/V heads, then row blocks (compact_item). With one split and K/V
+    // heads a multiple of 8, the items of XCD x (item % 8, the dispatch
+    // order) are those of heads x, x + 8, ... of every sequence, so each
+    // head's K and V are read through one L2 (varlen_mix 285 -> 278 us);
+    // every XCD still gets an equal share.
     const bool by_xcd = a.num_splits == 1 && a.Hkv % 8 == 0;
-    const int hper = by_xcd ? a.Hkv / 8 : a.Hkv;
-    long long k = by_xcd ? item / 8 : item;
-    int seq = -1, loc = 0, cnt_s = 1;
-    for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int sb = c0 + lane;
-      int cnt = 0;
-      if (sb < a.B) {
-        const int s0 = min(max(a.cu_q[sb], 0), a.Nq);
-        const int n = min(min(max(a.cu_q[sb + 1], s0), a.Nq) - s0, a.max_nq);
-        cnt = (int)(((long long)n * G + BM - 1) / BM);
-      }
-      long long incl = (long long)cnt * hper;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const long long y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const long long excl = incl - (long long)cnt * hper;
-      const unsigned long long hit = __ballot(k >= excl && k < incl);
-      if (hit != 0) {  // uniform: k is the same in every lane
-        const int l = __ffsll((long long)hit) - 1;
-        seq = c0 + l;
-        loc = (int)(k - __shfl(excl, l));
-        cnt_s = __shfl(cnt, l);
-        break;
-      }
-      k -= __shfl(incl, 63);
-    }
-    if (seq < 0) return;  // grid padding; uniform over the workgroup
-    b = __builtin_amdgcn_readfirstlane(seq);
-    loc = __builtin_amdgcn_readfirstlane(loc);
-    cnt_s = __builtin_amdgcn_readfirstlane(cnt_s);
-    hkv = by_xcd ? (int)(item % 8) + 8 * (loc / cnt_s) : loc / cnt_s;
-    const int level = loc % cnt_s;
+    int j, level, cnt_s;
+    if (!compact_item(item, a.cu_q, a.B, a.Nq, a.max_nq, G, BM, a.Hkv, by_xcd, lane, b, j, level, cnt_s))
+      return;  // grid padding; uniform over the workgroup
+    hkv = by_xcd ? (int)(item % 8) + 8 * j : j;
     rb = CAUSAL ? cnt_s - 1 - level : level;
   } else {
     const int nrb = (int)(((long long)a.max_nq * G + BM - 1) / BM);

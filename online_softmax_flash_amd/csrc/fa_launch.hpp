@@ -48,6 +48,7 @@ struct BwdKvArgs {
   int B, Hq, Hkv;
   int Nq, Nk;          // uniform: lengths; variable length: totals Tq, Tk
   int max_nq, max_nk;  // largest sequence lengths (grid sizing)
+  int compact;         // variable length: grids of the sequences' blocks only (B <= 256)
   long long rows;      // query rows: B*Hq*Nq, or Hq*Tq
   float c;             // scale * log2(e)
   float scale;
