@@ -54,9 +54,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   // last row block sees the most keys), so that the longest items start
   // first; with one split and pairs a multiple of 8, each XCD receives a
   // contiguous range of (batch, K/V head) pairs, whose K and V then stay in
-  // its L2. A variable-length batch goes pair by pair, heaviest row block
-  // first within each, over the row blocks its sequences actually have
-  // (compact grid): a grid of max_seqlen row blocks for every sequence spent
+  // its L2. A variable-length batch goes sequence by sequence, heaviest row
+  // blocks of every head first within each, over the row blocks its
+  // sequences actually have (compact grid): a grid of max_seqlen row blocks
+  // for every sequence spent
   // most of its workgroups on row blocks past the shorter sequences, each
   // dispatched only to read the offsets and exit.
   const long long wg = (long long)blockIdx.y * gridDim.x + blockIdx.x;
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   int b, hkv, rb;
   if (a.compact) {
     // Sequence s has ceil(n_s * G / BM) row blocks; items run over sequences,
-    // then K/V heads, then row blocks (compact_item). With one split and K/V
+    // then row-block levels (heaviest first), then K/V heads (compact_item).
+    // With one split and K/V
     // heads a multiple of 8, the items of XCD x (item % 8, the dispatch
     // order) are those of heads x, x + 8, ... of every sequence, so each
     // head's K and V are read through one L2 (varlen_mix 285 -> 278 us);
