@@ -124,9 +124,9 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *   cu_seqlens_q[b+1]-1 and key tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
  *   max_seqlen_q / max_seqlen_k: upper bounds of the per-sequence lengths (they
  *   size the launch). Offsets are clamped into [0, T] on the device, so any
- *   contents keep every access in bounds, but query tokens beyond
- *   max_seqlen_q in a sequence and tokens outside every sequence are left
- *   unspecified.
+ *   contents keep every access in bounds; results are defined for offsets
+ *   that rise from 0 to T with sequences of at most max_seqlen tokens, and
+ *   tokens outside every sequence are left unspecified.
  * num_splits: 1 = no split; 0 = the library's choice
  *   (flash_attn_fwd_kv_num_splits); at most 256.
  * workspace: caller-owned device buffer of flash_attn_fwd_kv_workspace_bytes(
@@ -134,7 +134,8 @@ int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *   the split count actually used; NULL is allowed when that is 1. Contents on
  *   entry ignored, on return unspecified.
  * Errors as flash_attn_fwd; FA_ERR_SHAPE also for num_splits outside
- * [0, 256], FA_ERR_WORKSPACE for a missing or short workspace.
+ * [0, 256] or a launch beyond 65536 x 65535 workgroups, FA_ERR_WORKSPACE
+ * for a missing or short workspace.
  */
 int flash_attn_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
