@@ -123,7 +123,8 @@ __device__ __forceinline__ SeqExtent seq_extent(const BwdKvArgs& a, int b) {
 // Work item of workgroup wg: (sequence b, head h, block kb) out of HB = H*B
 // (sequence, head) pairs times nb blocks, block-major (all pairs' block 0
 // first). Uniform batches use decode_block's order (each XCD a contiguous
-// range of pairs). Variable-length batches take pair wg % HB, so that with
+// range of pairs). Variable-length batches of more than 256 sequences (the
+// others take compact_item's grid) take pair wg % HB, so that with
 // round-robin dispatch over the 8 XCDs every XCD receives heads of every
 // sequence: a long sequence's work is spread over the chip instead of
 // landing on the XCD its pairs would occupy (every block of a pair still
