@@ -31,8 +31,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-source additions: MFMA accumulators in VGPRs for the bf16 forward and
 # the bf16 dQ kernel (fewer copies between the AGPR and VGPR files).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"fa_bwd_dq_bf16.hip": _VGPR_FORM, "fa_fwd_bf16.hip": _VGPR_FORM, "fa_fwd_kv_bf16.hip": _VGPR_FORM,
-               "fa_naive_bf16.hip": _VGPR_FORM}
+EXTRA_FLAGS = {"fa_bwd_dq_bf16.hip": _VGPR_FORM, "fa_bwd_fused_bf16.hip": _VGPR_FORM, "fa_fwd_bf16.hip": _VGPR_FORM,
+               "fa_fwd_kv_bf16.hip": _VGPR_FORM, "fa_naive_bf16.hip": _VGPR_FORM}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"]
 

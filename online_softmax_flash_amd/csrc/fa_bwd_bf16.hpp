@@ -178,16 +178,26 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(BwdKvArgs a) {
 // visible; LDS only, the next block's copies stay in flight), the products
 // that need P. Q, dO, l2 and D stream through LDS in double-buffered blocks,
 // over every query head of the K/V head's group. No atomics: deterministic.
+// LDS of the dK/dV kernel: two stages of (Q, dO, l2, D) and the P exchange.
+template <int D, int NP>
+struct DkdvLds {
+  static constexpr int RS = 2 * D + 16;  // padded LDS row bytes
+  static constexpr int TILE = 64 * RS;
+  static constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
+  static constexpr int PX = 2 * 64 * 16 * 4;  // P exchange bytes per pair: 2 subtiles x 64 lanes x 16 fp32
+  static constexpr int BYTES = 2 * STAGE + NP * PX;
+};
+
+// Work item wg of the dK/dV kernel, in `smem` (DkdvLds bytes, 1024-aligned).
 template <int D, int NP, bool CAUSAL>
-__global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdKvArgs& a, uint8_t* smem, int wg) {
   constexpr int NW = 2 * NP;
   constexpr int BKV = 32 * NP, BQ = 64;
-  constexpr int RS = 2 * D + 16;  // padded LDS row bytes
+  constexpr int RS = DkdvLds<D, NP>::RS;
   constexpr int NF = D / 16, NDT = D / 32;
-  constexpr int TILE = BQ * RS;
-  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
-  constexpr int PX = 2 * 64 * 16 * 4;  // P exchange bytes per pair: 2 subtiles x 64 lanes x 16 fp32
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + NP * PX];
+  constexpr int TILE = DkdvLds<D, NP>::TILE;
+  constexpr int STAGE = DkdvLds<D, NP>::STAGE;
+  constexpr int PX = DkdvLds<D, NP>::PX;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -204,11 +214,11 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
     // work) first; XCD x takes K/V heads x, x + 8, ... when they divide by 8.
     const bool by_xcd = a.Hkv % 8 == 0;
     int j, cnt;
-    if (!compact_item(blockIdx.x, a.cu_k, a.B, a.Nk, a.max_nk, 1, BKV, a.Hkv, by_xcd, lane, b, j, kb, cnt))
+    if (!compact_item(wg, a.cu_k, a.B, a.Nk, a.max_nk, 1, BKV, a.Hkv, by_xcd, lane, b, j, kb, cnt))
       return;  // grid padding; uniform over the workgroup
-    hkv = by_xcd ? (int)(blockIdx.x % 8) + 8 * j : j;
+    hkv = by_xcd ? wg % 8 + 8 * j : j;
   } else {
-    decode_item(blockIdx.x, a.Hkv, a.B, nkb_max, false, a.cu_q != nullptr, b, hkv, kb);  // key block 0 has the most work
+    decode_item(wg, a.Hkv, a.B, nkb_max, false, a.cu_q != nullptr, b, hkv, kb);  // key block 0 has the most work
   }
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
@@ -382,14 +392,23 @@ __global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
 // wave keeps 32 query rows of Q and dO as B-operand fragments in registers and
 // accumulates dQ^T over the visible key blocks; K and V stream through LDS in
 // blocks of 64 keys.
+// LDS of the dQ kernel: two stages of (K, V) blocks of 64 keys.
+template <int D>
+struct DqLds {
+  static constexpr int RS = 2 * D + 16;
+  static constexpr int TILE = 64 * RS;
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int BYTES = 2 * STAGE;
+};
+
+// Work item wg of the dQ kernel, in `smem` (DqLds bytes, 1024-aligned).
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
+__device__ __forceinline__ void bwd_dq_body(const BwdKvArgs& a, uint8_t* smem, int wg) {
   constexpr int BM = 32 * NW, BK = 64;
-  constexpr int RS = 2 * D + 16;
+  constexpr int RS = DqLds<D>::RS;
   constexpr int NF = D / 16, NDT = D / 32;
-  constexpr int TILE = BK * RS;
-  constexpr int STAGE = 2 * TILE;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int TILE = DqLds<D>::TILE;
+  constexpr int STAGE = DqLds<D>::STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // Wave index in a scalar register: the per-wave tests below (causal skip,
@@ -406,12 +425,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
     const int G = a.Hq / a.Hkv;
     const bool by_xcd = a.Hkv % 8 == 0;
     int j, level, cnt;
-    if (!compact_item(blockIdx.x, a.cu_q, a.B, a.Nq, a.max_nq, 1, BM, a.Hq, by_xcd, lane, b, j, level, cnt))
+    if (!compact_item(wg, a.cu_q, a.B, a.Nq, a.max_nq, 1, BM, a.Hq, by_xcd, lane, b, j, level, cnt))
       return;  // grid padding; uniform over the workgroup
-    hq = by_xcd ? ((int)(blockIdx.x % 8) + 8 * (j / G)) * G + j % G : j;
+    hq = by_xcd ? (wg % 8 + 8 * (j / G)) * G + j % G : j;
     qb = CAUSAL ? cnt - 1 - level : level;
   } else {
-    decode_item(blockIdx.x, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
+    decode_item(wg, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
   }
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
@@ -522,9 +541,37 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
   }
 }
 
+template <int D, int NP, bool CAUSAL>
+__global__ __launch_bounds__(128 * NP) void bwd_dkdv_bf16_kernel(BwdKvArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DkdvLds<D, NP>::BYTES];
+  bwd_dkdv_body<D, NP, CAUSAL>(a, smem, (int)blockIdx.x);
+}
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdKvArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DqLds<D>::BYTES];
+  bwd_dq_body<D, NW, CAUSAL>(a, smem, (int)blockIdx.x);
+}
+
+// dK/dV and dQ in one launch: workgroups [0, n_dkdv) take dK/dV items (the
+// heaviest first), the rest dQ items, so that dQ work fills the compute units
+// that the dK/dV kernel's last, longest items leave idle. The two are
+// independent (both read D and l2 only). n_dkdv is a multiple of 8, so the
+// XCD of a workgroup is that of its item index in either part.
+template <int D, int NP, int NWQ, bool CAUSAL>
+__global__ __launch_bounds__(128 * NP) void bwd_fused_bf16_kernel(BwdKvArgs a, int n_dkdv) {
+  static_assert(128 * NP == 64 * NWQ, "one workgroup size for both parts");
+  constexpr int L1 = DkdvLds<D, NP>::BYTES, L2 = DqLds<D>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L1 > L2 ? L1 : L2];
+  const int wg = (int)blockIdx.x;
+  if (wg < n_dkdv) bwd_dkdv_body<D, NP, CAUSAL>(a, smem, wg);
+  else bwd_dq_body<D, NWQ, CAUSAL>(a, smem, wg - n_dkdv);
+}
+
 // The dQ kernel's instances live in their own translation unit (built with
 // MFMA accumulators in VGPRs, which keeps it within two waves per SIMD).
 hipError_t launch_bwd_dq_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd_fused_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream);
 
 template <int D, int NPKV, bool CAUSAL>
 void launch_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
@@ -536,10 +583,12 @@ void launch_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
                      stream, a);
 }
 
+// D and l2, then the dK/dV kernel unless it runs in the fused launch.
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_prep_dkdv_bf16(const BwdKvArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_prep_dkdv_bf16(const BwdKvArgs& a, bool fused, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_prep_bf16_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+  if (fused) return hipGetLastError();
   // Pairs per workgroup: 4 (two waves per SIMD) while a wave's registers allow
   // it; at d = 256 a wave needs more than half the register file, so 2. At
   // d = 128 with the causal mask, 6 pairs (three waves per SIMD, 192 keys per
