@@ -7,12 +7,13 @@ namespace fa {
 
 hipError_t bwd_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream) {
   // dK/dV and dQ in one launch (dQ workgroups filling the compute units the
-  // dK/dV part's last items leave idle) at d = 256 and for variable-length
-  // batches: wide_4k 2.61 -> 2.48 ms, varlen_mix 1.04 -> 0.99 ms. Uniform
-  // batches at d <= 128 keep two launches: there the dK/dV kernel's six-pair
-  // form, which the fused launch's single workgroup size rules out, or the
-  // two smaller kernels measured faster (long_8k 1.82 against 1.94 ms).
-  const bool fused = d == 256 || a.cu_q != nullptr;
+  // dK/dV part's last items leave idle) at d = 256, for variable-length
+  // batches and for Nq != Nk: wide_4k 2.61 -> 2.48 ms, varlen_mix 1.04 ->
+  // 0.98 ms, chunk_2k_8k 0.87 -> 0.84 ms. Square batches at d <= 128 keep two
+  // launches: there the dK/dV kernel's six-pair form, which the fused
+  // launch's single workgroup size rules out, or the two smaller kernels
+  // measured faster (long_8k 1.82 against 1.94 ms, gqa_4k 3% slower fused).
+  const bool fused = d == 256 || a.cu_q != nullptr || a.Nq != a.Nk;
   hipError_t e;
   switch (d * 2 + (causal ? 1 : 0)) {
     case 64 * 2: e = launch_bwd_prep_dkdv_bf16<64, false>(a, fused, stream); break;
