@@ -467,7 +467,8 @@ def bench_kv(args, w):
     }
     if not args.no_backward and splits == 1:
         # The general backward over the same problem (o and lse from the
-        # forward above): one step = D and l2, the dK/dV and the dQ kernels.
+        # forward above): one step = D and l2, then dK/dV and dQ (one launch
+        # for variable-length batches, Nq != Nk and d = 256; two otherwise).
         do = torch.from_numpy(inp.do).to(torch.bfloat16).to(dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         wsb = torch.empty(max(fa.flash_attn_bwd_kv_workspace_bytes(rows, w.d), 256), dtype=torch.uint8, device=dev)
@@ -480,7 +481,9 @@ def bench_kv(args, w):
                 fa.flash_attn_bwd_kv(q, k, v, o, lse, do, dq, dk, dv, wsb, w.scale, w.causal)
 
         result["backward"] = time_backward(bstep, stream, 2.5 * flops, max(10, args.steps // 2))
-        result["backward"]["kernels"] = "bwd_prep_bf16_kernel, bwd_dkdv_bf16_kernel, bwd_dq_bf16_kernel"
+        fused = bool(w.lengths_seed) or w.Nq != w.Nk or w.d == 256
+        result["backward"]["kernels"] = ("bwd_prep_bf16_kernel, bwd_fused_bf16_kernel" if fused else
+                                         "bwd_prep_bf16_kernel, bwd_dkdv_bf16_kernel, bwd_dq_bf16_kernel")
 
     if not args.no_cpu_baseline:
         import oracle

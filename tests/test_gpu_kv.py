@@ -62,6 +62,31 @@ def test_kv_small_parity(shape, causal, splits):
     check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, f"{shape} causal={causal} splits={splits}")
 
 
+# Uniform batches at d = 128 whose row blocks see 4096 keys or more on
+# average, with 1024 packed rows or more and one split, run in eight-wave
+# workgroups (256 rows per block of keys): ragged rows and keys here.
+KV_EIGHT = [
+    # B, Hq, Hkv, Nq, Nk
+    (1, 4, 1, 300, 4500),
+    (2, 8, 2, 257, 4300),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", KV_EIGHT, ids=["x".join(map(str, s)) for s in KV_EIGHT])
+def test_kv_eight_wave_parity(shape, causal):
+    B, Hq, Hkv, Nq, Nk = shape
+    d = 128
+    announce(f"kv eight-wave shape={shape} causal={causal} seed=33")
+    inp = make_kv_inputs(B, Hq, Hkv, Nq, Nk, d, seed=33)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    o, lse = fa.attention_forward_kv(q, k, v, scale, causal, num_splits=1)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attn_fwd_materialised(inp.q, inp.k, inp.v, scale, causal)
+    check_rows(from_dev(o), from_dev(lse), O_ref, L_ref, f"{shape} causal={causal} eight waves")
+
+
 def test_kv_split_matches_unsplit():
     """Split keys change only the rounding order: lse to fp32 rounding, O to one bf16 step."""
     B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 2, 5000, 128
