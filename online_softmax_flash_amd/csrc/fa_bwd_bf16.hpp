@@ -432,6 +432,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdKvArgs& a, uint8_t* smem, i
   } else {
     decode_item(wg, a.Hq, a.B, nqb_max, CAUSAL, a.cu_q != nullptr, b, hq, qb);
   }
+  // Uniform by construction; said so, so that the sequence's extents are
+  // scalar loads and the masked-subtile test below stays a branch.
+  b = __builtin_amdgcn_readfirstlane(b);
+  hq = __builtin_amdgcn_readfirstlane(hq);
+  qb = __builtin_amdgcn_readfirstlane(qb);
   const SeqExtent sq = seq_extent(a, b);
   const int nq = sq.nq, nk = sq.nk;
   const int q0 = qb * BM;
@@ -506,14 +511,19 @@ __device__ __forceinline__ void bwd_dq_body(const BwdKvArgs& a, uint8_t* smem, i
       // key (l2 = -inf) is masked on every key.
       const bool masked = (CAUSAL && ks0 + 31 > qw0 + off) || ks0 + 32 > nk;
       float ds[16];
+      // Two copies of the loop, so that unmasked subtiles (most of them)
+      // carry no mask arithmetic.
+      if (masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
-        if (masked) {
+        for (int r = 0; r < 16; ++r) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
           const int key = ks0 + rho_row(r, h);
           if (key >= nk || (CAUSAL && key > qi + off)) pv = 0.f;
+          ds[r] = pv * (dp[r] - Di);
         }
-        ds[r] = pv * (dp[r] - Di);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2)) * (dp[r] - Di);
       }
       bf16x8 dsf[2];
       pack_frag(dsf[0], ds);
