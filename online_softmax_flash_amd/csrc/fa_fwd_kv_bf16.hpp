@@ -34,6 +34,28 @@
 
 namespace fa {
 
+// Copies of a K or V block: with several waves each lane's source offsets are
+// computed once (BlockDma, a few registers); a one-wave decoding workgroup
+// issues every instruction of the block and recomputes them per call
+// (LeanDma), which keeps its registers free.
+template <int D, int BN, int ROWB, int NW, bool HELD = (NW > 1)>
+struct KvDma {
+  BlockDma<D, BN, ROWB, NW> d;
+  __device__ __forceinline__ void init(int wave, int lane) { d.init(wave, lane); }
+  template <bool FULL>
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int) const {
+    d.template issue<FULL>(lds, g, valid, wave);
+  }
+};
+template <int D, int BN, int ROWB, int NW>
+struct KvDma<D, BN, ROWB, NW, false> {
+  __device__ __forceinline__ void init(int, int) {}
+  template <bool FULL>
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint16_t* g, int valid, int wave, int lane) const {
+    LeanDma<D, BN, ROWB, NW>::template issue<FULL>(lds, g, valid, wave, lane);
+  }
+};
+
 template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   using C = Bf16FwdCfg<D, BN, NW>;
@@ -140,19 +162,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + ((long long)b * k_bs + (long long)hkv * k_hs + ks) * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + ((long long)b * k_bs + (long long)hkv * k_hs + ks) * D;
 
-  using KDma = LeanDma<D, BN, C::KROW, NW>;
-  using VDma = LeanDma<D, BN, C::VROW, NW>;
+  KvDma<D, BN, C::KROW, NW> kdma;
+  KvDma<D, BN, C::VROW, NW> vdma;
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
   auto prefetch = [&](int kb) {
     uint8_t* st = smem + (kb & 1) * STAGE;
     const uint16_t* kg = K + (size_t)kb * BN * D;
     const uint16_t* vg = V + (size_t)kb * BN * D;
     const int valid = kend - kb * BN;
     if (valid >= BN) {
-      KDma::template issue<true>(st, kg, BN, wave, lane);
-      VDma::template issue<true>(st + C::KBYTES, vg, BN, wave, lane);
+      kdma.template issue<true>(st, kg, BN, wave, lane);
+      vdma.template issue<true>(st + C::KBYTES, vg, BN, wave, lane);
     } else {
-      KDma::template issue<false>(st, kg, valid, wave, lane);
-      VDma::template issue<false>(st + C::KBYTES, vg, valid, wave, lane);
+      kdma.template issue<false>(st, kg, valid, wave, lane);
+      vdma.template issue<false>(st + C::KBYTES, vg, valid, wave, lane);
     }
   };
   if (kb0 < kb_end) prefetch(kb0);
