@@ -511,9 +511,21 @@ __device__ __forceinline__ void bwd_dq_body(const BwdKvArgs& a, uint8_t* smem, i
       // key (l2 = -inf) is masked on every key.
       const bool masked = (CAUSAL && ks0 + 31 > qw0 + off) || ks0 + 32 > nk;
       float ds[16];
-      // Two copies of the loop, so that unmasked subtiles (most of them)
-      // carry no mask arithmetic.
-      if (masked) {
+      // Up to d = 128, two copies of the loop, so that unmasked subtiles
+      // (most of them) carry no mask arithmetic. At d = 256, where a wave
+      // holds 256 registers, the one loop below measured faster (the copies
+      // cost 6% at wide_4k).
+      if (D > 128) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
+          if (masked) {
+            const int key = ks0 + rho_row(r, h);
+            if (key >= nk || (CAUSAL && key > qi + off)) pv = 0.f;
+          }
+          ds[r] = pv * (dp[r] - Di);
+        }
+      } else if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
