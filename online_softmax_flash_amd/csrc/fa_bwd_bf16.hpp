@@ -68,6 +68,10 @@ __device__ __forceinline__ constexpr int rho_row(int r, int h) {
 // no wait for it before later LDS accesses or fences): callers wait (vmcnt)
 // and synchronise before the destination is read.
 __device__ __forceinline__ void dma_row_stats(uint8_t* lds, const float* g, int r0, int N, int lane) {
+  // The lane's row is recomputed at every call (a few instructions in one
+  // wave) rather than kept across the caller's loop, where a spilled copy
+  // reloaded from scratch would wait for the copies already in flight.
+  asm volatile("" : "+v"(lane));
   int r = r0 + 32 * (lane >> 5) + rho(lane & 31);
   r = r < N ? r : N - 1;
   const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(lds));
@@ -236,8 +240,20 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdKvArgs& a, uint8_t* smem,
   const int qb_start = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqs = nq > 0 ? max(nqb - qb_start, 0) : 0;
   const int nsteps = G * nqs;
+  // Copy offsets held per lane (BlockDma) up to four pairs. Six pairs (three
+  // waves per SIMD) have no registers to spare: there the held offsets were
+  // spilled, and every reload waited for the copies already in flight, so
+  // they are recomputed per call (LeanDma).
+  constexpr bool HELD = NP <= 4;
   BlockDma<D, BQ, RS, NW> dma;
-  dma.init(wave, lane);
+  if constexpr (HELD) dma.init(wave, lane);
+  auto copy_tile = [&](auto full_tag, uint8_t* dst, const uint16_t* src, int valid) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    if constexpr (HELD)
+      dma.template issue<FULL>(dst, src, valid, wave);
+    else
+      LeanDma<D, BQ, RS, NW>::template issue<FULL>(dst, src, valid, wave, lane);
+  };
   auto prefetch = [&](int i) {
     const int g = i / nqs, q0 = (qb_start + i % nqs) * BQ;
     const long long qr = sq.qrow0(b, hkv * G + g);
@@ -245,11 +261,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdKvArgs& a, uint8_t* smem,
     const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + (qr + q0) * D;
     const uint16_t* Og = static_cast<const uint16_t*>(a.dout) + (qr + q0) * D;
     if (q0 + BQ <= nq) {
-      dma.template issue<true>(st, Qg, BQ, wave);
-      dma.template issue<true>(st + TILE, Og, BQ, wave);
+      copy_tile(std::true_type{}, st, Qg, BQ);
+      copy_tile(std::true_type{}, st + TILE, Og, BQ);
     } else {
-      dma.template issue<false>(st, Qg, nq - q0, wave);
-      dma.template issue<false>(st + TILE, Og, nq - q0, wave);
+      copy_tile(std::false_type{}, st, Qg, nq - q0);
+      copy_tile(std::false_type{}, st + TILE, Og, nq - q0);
     }
     if (wave == 0) dma_row_stats(st + 2 * TILE, a.l2 + qr, q0, nq, lane);
     if (wave == NW - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qr, q0, nq, lane);
