@@ -219,11 +219,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
     bool keep[NKT][16];
     auto mask = [&] {
       if constexpr (MASKED) {
+        const int lim = klim - k0 - 8 * h;  // key k0 + 32 kt + sigma_row(e, h) is visible iff <= klim
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            keep[kt][e] = k0 + 32 * kt + sigma_row(e, h) <= klim;
+            keep[kt][e] = 32 * kt + sigma_row(e, 0) <= lim;
             if (!keep[kt][e]) s[kt][e] = -INFINITY;
           }
       }
