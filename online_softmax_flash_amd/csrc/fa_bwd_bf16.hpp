@@ -240,21 +240,24 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdKvArgs& a, uint8_t* smem,
   const int qb_start = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqs = nq > 0 ? max(nqb - qb_start, 0) : 0;
   const int nsteps = G * nqs;
-  // Copy offsets held per lane (BlockDma) up to four pairs. Six pairs (three
-  // waves per SIMD) have no registers to spare: there the held offsets were
-  // spilled, and every reload waited for the copies already in flight, so
-  // they are recomputed per call (LeanDma).
-  constexpr bool HELD = NP <= 4;
-  BlockDma<D, BQ, RS, NW> dma;
-  if constexpr (HELD) dma.init(wave, lane);
+  // The dS waves issue each step's copies (they wait for P at the second
+  // barrier anyway); the P waves go straight on to their score products.
+  // Copy offsets held per lane (BlockDma) with four pairs; recomputed per
+  // call (LeanDma) with two (d = 256) or six, whose waves have no registers
+  // to spare.
+  constexpr bool HELD = NP == 4;
+  const int cw = wave - NP;  // index among the dS waves; < 0 for the P waves
+  BlockDma<D, BQ, RS, NP> dma;
+  if constexpr (HELD) dma.init(cw >= 0 ? cw : 0, lane);
   auto copy_tile = [&](auto full_tag, uint8_t* dst, const uint16_t* src, int valid) {
     constexpr bool FULL = decltype(full_tag)::value;
     if constexpr (HELD)
-      dma.template issue<FULL>(dst, src, valid, wave);
+      dma.template issue<FULL>(dst, src, valid, cw);
     else
-      LeanDma<D, BQ, RS, NW>::template issue<FULL>(dst, src, valid, wave, lane);
+      LeanDma<D, BQ, RS, NP>::template issue<FULL>(dst, src, valid, cw, lane);
   };
   auto prefetch = [&](int i) {
+    if (pwave) return;
     const int g = i / nqs, q0 = (qb_start + i % nqs) * BQ;
     const long long qr = sq.qrow0(b, hkv * G + g);
     uint8_t* st = smem + (i & 1) * STAGE;
@@ -267,8 +270,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdKvArgs& a, uint8_t* smem,
       copy_tile(std::false_type{}, st, Qg, nq - q0);
       copy_tile(std::false_type{}, st + TILE, Og, nq - q0);
     }
-    if (wave == 0) dma_row_stats(st + 2 * TILE, a.l2 + qr, q0, nq, lane);
-    if (wave == NW - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qr, q0, nq, lane);
+    if (cw == 0) dma_row_stats(st + 2 * TILE, a.l2 + qr, q0, nq, lane);
+    if (cw == NP - 1) dma_row_stats(st + 2 * TILE + BQ * 4, a.dsum + qr, q0, nq, lane);
   };
   if (nsteps > 0) prefetch(0);
 
