@@ -8,8 +8,8 @@ namespace fa {
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int N, int d, float c, int causal, hipStream_t stream) {
   const FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, c};
-  // d = 64: 16-wave workgroups (512 rows, four waves per SIMD; the compiler
-  // keeps a wave within 128 registers with 12-17 spilled) on long sequences
+  // d = 64: 16-wave workgroups (512 rows, four waves per SIMD, 128 registers
+  // a wave) on long sequences
   // with a query block of 512 rows for every CU or more: 9-11% faster at
   // N = 2048-8192 than 8 waves, whose softmax work per product is twice that
   // at d = 128; slower on short or few sequences, which keep 8 waves.

@@ -264,18 +264,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     return x;
   };
 
-  // With 8 waves the block copies are issued by the last four only, one per
-  // SIMD (the SIMD's other wave goes on computing while these stall on the
-  // issue): 2% faster at long_8k, 1-3% on shorter shapes, than every wave
-  // issuing its share; the first four waves as the issuers gained less
-  // (0.8%). With 16 waves (d = 64, 128 registers a wave) the offsets of a
-  // four-wave share do not fit, so all waves issue.
-  constexpr int CW = NW == 8 ? 4 : NW;
+  // With 8 or 16 waves the block copies are issued by the last four only,
+  // one per SIMD (the SIMD's other waves go on computing while these stall
+  // on the issue): 2% faster at long_8k, 1-3% on shorter shapes, than every
+  // wave issuing its share; the first four waves as the issuers gained less
+  // (0.8%). With 16 waves (d = 64, 128 registers a wave) the four issuers
+  // recompute their offsets per call (LeanDma), which also ends the
+  // compiler's spills there: d = 64 causal 2.6-9% faster.
+  constexpr int CW = NW >= 8 ? 4 : NW;
   const int cwave = wave - (NW - CW);  // index among the issuing waves; < 0 for the others
+  constexpr bool LEAN = NW > 8;
   BlockDma<D, BN, C::KROW, CW> kdma;
   BlockDma<D, BN, C::VROW, CW> vdma;
-  kdma.init(cwave >= 0 ? cwave : 0, lane);
-  vdma.init(cwave >= 0 ? cwave : 0, lane);
+  if constexpr (!LEAN) {
+    kdma.init(cwave >= 0 ? cwave : 0, lane);
+    vdma.init(cwave >= 0 ? cwave : 0, lane);
+  }
   // Block kb of item x into LDS stage st (0 or 1).
   auto copy_block = [&](const Item& x, int kb, int st_idx) {
     uint8_t* st = smem + st_idx * STAGE;
@@ -283,6 +287,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t* kg = static_cast<const uint16_t*>(a.k) + off;
     const uint16_t* vg = static_cast<const uint16_t*>(a.v) + off;
     if (cwave < 0) return;
+    if constexpr (LEAN) {
+      if (kb < nfull_rows) {
+        LeanDma<D, BN, C::KROW, CW>::template issue<true>(st, kg, BN, cwave, lane);
+        LeanDma<D, BN, C::VROW, CW>::template issue<true>(st + C::KBYTES, vg, BN, cwave, lane);
+      } else {
+        LeanDma<D, BN, C::KROW, CW>::template issue<false>(st, kg, N - kb * BN, cwave, lane);
+        LeanDma<D, BN, C::VROW, CW>::template issue<false>(st + C::KBYTES, vg, N - kb * BN, cwave, lane);
+      }
+      return;
+    }
     if (kb < nfull_rows) {
       kdma.template issue<true>(st, kg, BN, cwave);
       vdma.template issue<true>(st + C::KBYTES, vg, BN, cwave);
@@ -372,12 +386,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
     bool keep[NKT][16];
     auto mask = [&] {
       if constexpr (MASKED) {
+        // Key k0 + 32 kt + sigma_row(r, h) is visible iff it is < N and
+        // (causal) <= qi: one compare of a constant against the lane's limit.
+        const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - k0 - 8 * h;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kt + sigma_row(r, h);
-            keep[kt][r] = key < N && (!CAUSAL || key <= qi);
+            keep[kt][r] = 32 * kt + sigma_row(r, 0) <= lim;
             if (!keep[kt][r]) s[kt][r] = -INFINITY;
           }
       }
