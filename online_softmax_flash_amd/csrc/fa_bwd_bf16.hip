@@ -7,13 +7,15 @@ namespace fa {
 
 hipError_t bwd_bf16(const BwdKvArgs& a, int d, int causal, hipStream_t stream) {
   // dK/dV and dQ in one launch (dQ workgroups filling the compute units the
-  // dK/dV part's last items leave idle) at d = 256, for variable-length
-  // batches and for Nq != Nk: wide_4k 2.61 -> 2.48 ms, varlen_mix 1.04 ->
-  // 0.98 ms, chunk_2k_8k 0.87 -> 0.84 ms. Square batches at d <= 128 keep two
-  // launches: there the dK/dV kernel's six-pair form, which the fused
-  // launch's single workgroup size rules out, or the two smaller kernels
-  // measured faster (long_8k 1.82 against 1.94 ms, gqa_4k 3% slower fused).
-  const bool fused = d == 256 || a.cu_q != nullptr || a.Nq != a.Nk;
+  // dK/dV part's last items leave idle), except where the dK/dV kernel takes
+  // its six-pair form (causal d = 128 grids of four or more rounds), which
+  // the fused launch's single workgroup size rules out: long_8k 1.79 ms in
+  // two launches against 1.85 fused. Fused: wide_4k 2.61 -> 2.48 ms,
+  // varlen_mix 1.04 -> 0.98 ms, chunk_2k_8k 0.87 -> 0.84 ms, bwd_4k -2.8%
+  // (-1.5% not causal), gqa_4k unchanged.
+  const long long wgs6 = (long long)((a.max_nk + 191) / 192) * a.Hkv * a.B;
+  const bool six = d == 128 && causal && a.cu_q == nullptr && wgs6 >= 4LL * device_cu_count();
+  const bool fused = !six;
   hipError_t e;
   switch (d * 2 + (causal ? 1 : 0)) {
     case 64 * 2: e = launch_bwd_prep_dkdv_bf16<64, false>(a, fused, stream); break;
