@@ -238,19 +238,47 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* p) {
 // (rows cu[s] .. cu[s+1], clamped into [0, total] and to max_len rows, as the
 // kernels clamp them) has cnt_s = ceil(len_s * mult / blk) blocks; the items
 // run over sequences, then over block levels, then over the heads of the list
-// (so that a sequence's heaviest blocks of every head come first). With
+// (so that a sequence's heaviest blocks of every head come first). Up to 64
+// sequences go longest first (ties in batch order), more in batch order. With
 // xcd_heads (H a multiple of 8 and one item per workgroup in dispatch order),
 // the items of XCD x = item % 8 are those of heads x, x + 8, ... only; the
 // returned head index j then counts those heads (head = x + 8 * j). Every lane
-// of the wave finds the sequence by a prefix sum over chunks of 64 sequences
-// and returns the same, wave-uniform, values. False: grid padding.
+// of the wave finds the sequence (by the item counts of the sequences ahead
+// of each lane's, or by a prefix sum over chunks of 64 sequences) and returns
+// the same, wave-uniform, values. False: grid padding.
 __device__ __forceinline__ bool compact_item(long long item, const int* cu, int B, int total, int max_len, int mult,
                                              int blk, int H, bool xcd_heads, int lane, int& seq, int& j, int& level,
                                              int& cnt_seq) {
   const int hper = xcd_heads ? H / 8 : H;
   long long k = xcd_heads ? item / 8 : item;
   int s_found = -1, loc = 0, cnt_found = 1;
-  for (int c0 = 0; c0 < B; c0 += 64) {
+  if (B <= 64) {
+    // Longest first, so that the longest sequences' items, which set the
+    // critical path, start first (16 sequences of log-uniform lengths in
+    // 64..4096 listed in random order: forward +1.8%, backward +0.8%; a batch
+    // already in that order pays for the ranking, 1.5%).
+    int n = -1, cnt = 0;
+    if (lane < B) {
+      const int s0 = min(max(cu[lane], 0), total);
+      n = min(min(max(cu[lane + 1], s0), total) - s0, max_len);
+      cnt = (int)(((long long)n * mult + blk - 1) / blk);
+    }
+    int ahead = 0;  // blocks of the sequences ahead of this lane's
+    for (int t = 0; t < B; ++t) {
+      const int nt = __builtin_amdgcn_readlane(n, t);
+      const int ct = __builtin_amdgcn_readlane(cnt, t);
+      ahead += ((nt > n) | ((nt == n) & (t < lane))) ? ct : 0;
+    }
+    const long long excl = (long long)ahead * hper;
+    const unsigned long long hit = __ballot(lane < B && k >= excl && k < excl + (long long)cnt * hper);
+    if (hit != 0) {
+      const int l = __ffsll((long long)hit) - 1;
+      s_found = l;
+      loc = (int)(k - __shfl(excl, l));
+      cnt_found = __shfl(cnt, l);
+    }
+  }
+  for (int c0 = 0; c0 < B && B > 64; c0 += 64) {
     const int sb = c0 + lane;
     int cnt = 0;
     if (sb < B) {
