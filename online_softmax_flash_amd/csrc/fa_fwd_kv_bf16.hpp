@@ -76,8 +76,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kv_bf16_kernel(KvArgs a) {
   // last row block sees the most keys), so that the longest items start
   // first; with one split and pairs a multiple of 8, each XCD receives a
   // contiguous range of (batch, K/V head) pairs, whose K and V then stay in
-  // its L2. A variable-length batch goes sequence by sequence, heaviest row
-  // blocks of every head first within each, over the row blocks its
+  // its L2. A variable-length batch goes sequence by sequence (up to 64
+  // sequences: the longest first), heaviest row blocks of every head first
+  // within each, over the row blocks its
   // sequences actually have (compact grid): a grid of max_seqlen row blocks
   // for every sequence spent
   // most of its workgroups on row blocks past the shorter sequences, each
