@@ -208,3 +208,55 @@ def test_bwd_varlen_many_sequences(n_seq):
     assert_close(from_dev(dq), rq, "bf16", f"dQ n_seq={n_seq}", storage_rounding=True)
     assert_close(from_dev(dk), rk, "bf16", f"dK n_seq={n_seq}", storage_rounding=True)
     assert_close(from_dev(dv), rv, "bf16", f"dV n_seq={n_seq}", storage_rounding=True)
+
+
+ORDER = [(8, 8, 128, True), (4, 2, 64, False)]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,causal", ORDER, ids=["h8-d128-causal", "gqa-d64-noncausal"])
+def test_varlen_sequence_order_invariance(Hq, Hkv, d, causal):
+    """The kernels take the sequences of a variable-length batch (up to 64)
+    longest first, whatever order the batch lists them in. Listing the same
+    sequences in another order must leave every sequence's O, lse, dQ, dK and
+    dV bit for bit unchanged: the work items differ only in the order they run
+    in. Lengths with ties, an empty sequence and several multi-block ones;
+    queries and keys of different lengths when not causal."""
+    rng = np.random.default_rng(91)
+    lq = np.array([300, 17, 300, 0, 129, 64, 1000, 65, 300, 1, 511, 96], dtype=np.int64)
+    lk = lq.copy() if causal else rng.integers(1, 700, size=lq.size)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"varlen order invariance Hq={Hq} Hkv={Hkv} d={d} causal={causal} seed=92")
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    inp = make_varlen_inputs(Hq, Hkv, cu_q, cu_k, d, seed=92, with_dout=True)
+
+    def run(order):
+        sq = [slice(int(cu_q[s]), int(cu_q[s + 1])) for s in order]
+        sk = [slice(int(cu_k[s]), int(cu_k[s + 1])) for s in order]
+        q = np.concatenate([inp.q[:, x] for x in sq], axis=1)
+        do = np.concatenate([inp.do[:, x] for x in sq], axis=1)
+        k = np.concatenate([inp.k[:, x] for x in sk], axis=1)
+        v = np.concatenate([inp.v[:, x] for x in sk], axis=1)
+        cq = torch.tensor(np.concatenate([[0], np.cumsum(lq[order])]), dtype=torch.int32, device="cuda")
+        ck = torch.tensor(np.concatenate([[0], np.cumsum(lk[order])]), dtype=torch.int32, device="cuda")
+        qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+        mq, mk = int(lq.max()), int(lk.max())
+        o, lse = fa.attention_forward_varlen(qd, kd, vd, cq, ck, mq, mk, scale, causal, num_splits=1)
+        dq, dk, dv = fa.attention_backward_varlen(qd, kd, vd, o, lse, dod, cq, ck, mq, mk, scale, causal)
+        torch.cuda.synchronize()
+        out = {}
+        oq = np.concatenate([[0], np.cumsum(lq[order])])
+        ok = np.concatenate([[0], np.cumsum(lk[order])])
+        for i, s in enumerate(order):
+            a, b = int(oq[i]), int(oq[i + 1])
+            c, e = int(ok[i]), int(ok[i + 1])
+            out[int(s)] = (o[:, a:b].view(torch.int16).cpu(), lse[:, a:b].cpu(), dq[:, a:b].view(torch.int16).cpu(),
+                           dk[:, c:e].view(torch.int16).cpu(), dv[:, c:e].view(torch.int16).cpu())
+        return out
+
+    base = run(np.arange(lq.size))
+    for order in (np.arange(lq.size)[::-1].copy(), rng.permutation(lq.size), np.argsort(-lq, kind="stable")):
+        got = run(order)
+        for s in range(lq.size):
+            for name, x, y in zip(("O", "lse", "dQ", "dK", "dV"), base[s], got[s]):
+                assert torch.equal(x, y), f"sequence {s}: {name} depends on the batch order {order.tolist()}"

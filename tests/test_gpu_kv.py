@@ -226,11 +226,11 @@ MANY = [(64, 4, 2), (64, 16, 8), (256, 4, 2), (300, 4, 2)]
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_many_sequences(n_seq, Hq, Hkv, causal):
     """Many short sequences (0-150 queries, 0-200 keys each, seeded): the
-    compact grid of the sequences' row blocks, found by a prefix sum over
-    chunks of 64 sequences (64: one chunk; 256: four, the largest batch that
-    takes it; 8 K/V heads: the order that gives each XCD its own heads) and
-    the full grid of max_seqlen row blocks per sequence (300 sequences);
-    every row against the oracle."""
+    compact grid of the sequences' row blocks (64 sequences: ranked longest
+    first; 256: found by a prefix sum over four chunks of 64, the largest
+    batch that takes the compact grid; 8 K/V heads: the order that gives each
+    XCD its own heads) and the full grid of max_seqlen row blocks per
+    sequence (300 sequences); every row against the oracle."""
     rng = np.random.default_rng(1000 + n_seq)
     lq = rng.integers(0, 151, size=n_seq)
     lk = rng.integers(0, 201, size=n_seq)
