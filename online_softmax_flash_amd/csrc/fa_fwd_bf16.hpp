@@ -237,11 +237,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   const int nkb = (N + BN - 1) / BN;
   const int nfull_rows = N / BN;  // blocks with all BN rows inside [0, N)
 
-  // Work items (query block, head, batch), longest first (decode_block). The
-  // grid holds one workgroup per CU; workgroup w takes items w, then in every
-  // other round the mirror image of w among the workgroups of its XCD, so
-  // that long and short items pair up (balanced causal work) and every item
-  // runs on the XCD the head order assigns it (L2 reuse of K and V).
+  // Work items (query block, head, batch). The grid holds one workgroup per
+  // CU; workgroup w takes items w, then in every other round the mirror
+  // image of w among the workgroups of its XCD, so that long and short items
+  // pair up (balanced causal work). Item i runs on XCD i mod 8. Persistent
+  // workgroups of up to 8 waves take the (batch, head) pairs one at a time,
+  // all of a pair's query blocks together (longest first), each XCD its own
+  // eighth of the pairs when their count is a multiple of 8: the CUs of an
+  // XCD then stream the same K and V through its L2 at the same time
+  // (long_8k: 250 instead of 485 MB fetched per launch, time unchanged).
+  // 16-wave workgroups (where the longer decode costs spills) and one-item
+  // workgroups keep decode_block's order: level by level, longest first,
+  // each XCD a contiguous range of pairs.
   const int G = (int)gridDim.x, n_items = nqb * a.Hq * a.B;
   auto item_of = [&](int r) {
     const int w = (int)blockIdx.x;
@@ -254,7 +261,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdArgs a) {
   auto make_item = [&](int it) {
     Item x;
     int qb;
-    decode_block(it, a.Hq, a.B, nqb, CAUSAL, x.b, x.hq, qb);
+    if constexpr (PERSIST && NW <= 8) {  // (16-wave workgroups at 128 registers: decode_block)
+      // XCD x takes pairs x * HB/8 .. (x+1) * HB/8 - 1 (HB a multiple of 8;
+      // otherwise the items of a pair simply follow one another).
+      const unsigned HB = (unsigned)(a.Hq * a.B), X = HB % 8u == 0 ? 8u : 1u;
+      const unsigned xcd = (unsigned)it % X, j = (unsigned)it / X;
+      const unsigned p = xcd * (HB / X) + j / (unsigned)nqb, level = j % (unsigned)nqb;
+      x.b = (int)(p / (unsigned)a.Hq);
+      x.hq = (int)(p % (unsigned)a.Hq);
+      qb = CAUSAL ? nqb - 1 - (int)level : (int)level;
+    } else {
+      decode_block(it, a.Hq, a.B, nqb, CAUSAL, x.b, x.hq, qb);
+    }
     x.q0 = qb * BM;
     const int q_last = min(x.q0 + BM, N) - 1;
     x.kb_end = CAUSAL ? min(nkb, q_last / BN + 1) : nkb;
